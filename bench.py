@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused conv tensor product on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of synthetic input that is
+already resident in HBM.  Default workload (`l3fb`): lmax = 3, N = 16384
+nodes, C = 128 channels (N*C = 2^21), Poisson(45) in-degrees, Y given,
+forward (CSR, deterministic) + backward (dx, dw, dY).  Other workloads:
+`l2fwd` (lmax 2, N = 32768, forward), `sweepC` (lmax 2, N = 2^22/C, forward,
+CSR and atomic timed, C in 64..1024), `water` (1503 atoms, 83,325 edges,
+two lmax-3 layers forward + backward to edge vectors), `tiny`.
+
+Throughput is algorithmic bytes / time (the byte model counts every array
+the method must touch once: w, Y or vec, index arrays, x and G once, outputs
+once) and edges / time.  Kernel times come from HIP events recorded on the
+stream the kernels run on.  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv TP fwd/bwd effective GB/s (% of MI355X HBM peak); edges/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def fwd_bytes(N, E, C, D1, D2, D3, P, S):
+    return 4 * (E * P * C + E * S + E + (N + 1) + N * C * D1 + N * C * D3)
+
+
+def bwd_bytes(N, E, C, D1, D2, D3, P, S):
+    return 4 * (2 * E * P * C + 2 * E * S + 2 * E + (N + 1) + 2 * N * C * D1 + N * C * D3)
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tensor_product_message_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """Per-kernel HIP events on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        r = fn()
+        ev1.record()
+        self.pairs.setdefault(name, []).append((ev0, ev1))
+        return r
+
+    def mean_ms(self, name):
+        p = self.pairs.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in p) / len(p) if p else float("nan")
+
+    def reset(self):
+        self.pairs = {}
+
+
+# ------------------------------------------------------------ workloads
+
+
+def make_poisson(ctp, torch, dev, n, c, L, y_mode, with_bwd, seed=0):
+    from workloads import gen
+    d = gen.poisson_full(n, c, L, dev, seed=seed, need_grad=with_bwd)
+    g = ctp.Graph(n, torch.as_tensor(d["row_ptr"]).to(dev), torch.as_tensor(d["senders"]).to(dev))
+    vec = torch.as_tensor(d["vec"]).to(dev)
+    y = ctp.spherical_harmonics(vec, L) if y_mode == ctp.Y_GIVEN else vec
+    if with_bwd:
+        g.transpose  # built once per static graph, outside the timed region
+    torch.cuda.synchronize()
+    return d, g, y
+
+
+def shape_of(d, ctp, L, y_mode):
+    N, E, C = d["n_nodes"], d["n_edges"], d["channels"]
+    D = ctp.dim(L)
+    P = ctp.num_paths(L)
+    S = D if y_mode == ctp.Y_GIVEN else 3
+    return N, E, C, D, D, D, P, S
+
+
+def workload_l3fb(ctp, torch, dev, args):
+    L, y_mode = 3, (ctp.VEC_GIVEN if args.vec else ctp.Y_GIVEN)
+    d, g, y = make_poisson(ctp, torch, dev, 16384, 128, L, y_mode, True)
+    x, w, G = d["x"], d["w"], d["grad_out"]
+    out = torch.empty_like(x)
+    dx, dw, dy = torch.empty_like(x), torch.empty_like(w), torch.empty_like(y)
+    shp = shape_of(d, ctp, L, y_mode)
+
+    def step(t):
+        t.run("fwd", lambda: ctp.conv_tp_fwd(x, y, w, g, L, y_mode, out=out))
+        t.run("bwd", lambda: ctp.conv_tp_bwd(G, x, y, w, g, L, y_mode, dx=dx, dw=dw, dy=dy))
+
+    kb = {"fwd": fwd_bytes(*shp), "bwd": bwd_bytes(*shp)}
+    cfg = {"workload": f"lmax=3 conv TP forward+backward, N=16384, C=128, E={shp[1]}, "
+                       f"Poisson(45) in-degree, {'vec' if args.vec else 'Y'} given, fp32",
+           "n_nodes": shp[0], "n_edges": shp[1], "channels": 128, "lmax": 3,
+           "y_mode": "vec" if args.vec else "Y", "paths": shp[6]}
+    return dict(step=step, kernel_bytes=kb, dominant="bwd", edges=shp[1], cfg=cfg,
+                cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=True))
+
+
+def workload_l2fwd(ctp, torch, dev, args):
+    L, y_mode = 2, ctp.Y_GIVEN
+    d, g, y = make_poisson(ctp, torch, dev, 32768, 128, L, y_mode, False)
+    x, w = d["x"], d["w"]
+    out = torch.empty_like(x)
+    shp = shape_of(d, ctp, L, y_mode)
+
+    def step(t):
+        t.run("fwd", lambda: ctp.conv_tp_fwd(x, y, w, g, L, y_mode, out=out))
+
+    cfg = {"workload": f"lmax=2 conv TP forward, N=32768, C=128, E={shp[1]}, Poisson(45), Y given, fp32",
+           "n_nodes": shp[0], "n_edges": shp[1], "channels": 128, "lmax": 2, "paths": shp[6]}
+    return dict(step=step, kernel_bytes={"fwd": fwd_bytes(*shp)}, dominant="fwd", edges=shp[1], cfg=cfg,
+                cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=False))
+
+
+def workload_sweep(ctp, torch, dev, args):
+    L, y_mode, c = 2, ctp.Y_GIVEN, args.channels
+    n = (1 << 22) // c
+    d, g, y = make_poisson(ctp, torch, dev, n, c, L, y_mode, False)
+    x, w = d["x"], d["w"]
+    out, out2 = torch.empty_like(x), torch.empty_like(x)
+    shp = shape_of(d, ctp, L, y_mode)
+
+    def step(t):
+        t.run("fwd", lambda: ctp.conv_tp_fwd(x, y, w, g, L, y_mode, ctp.ALGO_CSR, out=out))
+        t.run("fwd_atomic", lambda: ctp.conv_tp_fwd(x, y, w, g, L, y_mode, ctp.ALGO_ATOMIC, out=out2))
+
+    fb = fwd_bytes(*shp)
+    cfg = {"workload": f"channel sweep lmax=2 forward, C={c}, N={n}, E={shp[1]}, Poisson(45), "
+                       "CSR and atomic both timed, fp32",
+           "n_nodes": n, "n_edges": shp[1], "channels": c, "lmax": 2, "paths": shp[6]}
+    return dict(step=step, kernel_bytes={"fwd": fb, "fwd_atomic": fb}, dominant="fwd", edges=shp[1], cfg=cfg,
+                cpu=None, value_kernels=("fwd",))
+
+
+def workload_water(ctp, torch, dev, args):
+    from workloads import gen
+    L, y_mode = 3, ctp.VEC_GIVEN
+    wb = gen.water_box(seed=0, device=dev)
+    n = wb["n_nodes"]
+    g = ctp.Graph(n, torch.as_tensor(wb["row_ptr"]).to(dev), torch.as_tensor(wb["senders"]).to(dev))
+    g.transpose
+    v = torch.as_tensor(wb["vec"]).to(dev)
+    x0 = torch.as_tensor(wb["x"]).to(dev)
+    G = torch.as_tensor(wb["grad_out"]).to(dev)
+    w1, w2 = wb["w1"], wb["w2"]
+    h1, h2 = torch.empty_like(x0), torch.empty_like(x0)
+    dh1, dx0 = torch.empty_like(x0), torch.empty_like(x0)
+    dw1, dw2 = torch.empty_like(w1), torch.empty_like(w2)
+    dv1, dv2 = torch.empty_like(v), torch.empty_like(v)
+    torch.cuda.synchronize()
+
+    def step(t):
+        t.run("fwd1", lambda: ctp.conv_tp_fwd(x0, v, w1, g, L, y_mode, out=h1))
+        t.run("fwd2", lambda: ctp.conv_tp_fwd(h1, v, w2, g, L, y_mode, out=h2))
+        t.run("bwd2", lambda: ctp.conv_tp_bwd(G, h1, v, w2, g, L, y_mode, dx=dh1, dw=dw2, dy=dv2))
+        t.run("bwd1", lambda: ctp.conv_tp_bwd(dh1, x0, v, w1, g, L, y_mode, dx=dx0, dw=dw1, dy=dv1))
+
+    E = wb["n_edges"]
+    shp = (n, E, 128, 16, 16, 16, ctp.num_paths(L), 3)
+    kb = {"fwd1": fwd_bytes(*shp), "fwd2": fwd_bytes(*shp), "bwd1": bwd_bytes(*shp), "bwd2": bwd_bytes(*shp)}
+    cfg = {"workload": f"water-box-shaped step: 1503 atoms, {E} edges (10% zero-weight padding), "
+                       "C=128, lmax=3, vec given, two layers forward + backward to edge vectors, fp32",
+           "n_nodes": n, "n_edges": E, "channels": 128, "lmax": 3, "layers": 2}
+    return dict(step=step, kernel_bytes=kb, dominant="bwd1", edges=E, cfg=cfg, cpu=None)
+
+
+def workload_tiny(ctp, torch, dev, args):
+    from workloads import gen
+    d = gen.tiny()
+    L, y_mode = 1, ctp.VEC_GIVEN
+    g = ctp.Graph(64, torch.as_tensor(d["row_ptr"]).to(dev), torch.as_tensor(d["senders"]).to(dev))
+    g.transpose
+    x, w, G, v = (torch.as_tensor(d[k]).to(dev) for k in ("x", "w", "grad_out", "vec"))
+    shp = (64, d["n_edges"], 16, 4, 4, 4, 5, 3)
+
+    def step(t):
+        t.run("fwd", lambda: ctp.conv_tp_fwd(x, v, w, g, L, y_mode))
+        t.run("bwd", lambda: ctp.conv_tp_bwd(G, x, v, w, g, L, y_mode))
+
+    cfg = {"workload": "tiny: 64 nodes, 16 channels, lmax=1, 16 distinct senders, vec given, fp32"}
+    return dict(step=step, kernel_bytes={"fwd": fwd_bytes(*shp), "bwd": bwd_bytes(*shp)}, dominant="bwd",
+                edges=d["n_edges"], cfg=cfg, cpu=None)
+
+
+WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
+             "water": workload_water, "tiny": workload_tiny}
+
+
+# ------------------------------------------------------------ CPU baseline (oracle)
+
+
+def cpu_baseline(spec, sample_nodes):
+    """Time the fp64 oracle (C edge loop, OpenMP) on a bounded sample of the
+    same workload and scale to the benchmark's units."""
+    import numpy as np
+    from oracle import convtp as oc
+    from oracle import graph as og
+    from oracle import sh as osh
+
+    d, L, shp, fb = spec["d"], spec["L"], spec["shp"], spec["fb"]
+    N, E = shp[0], shp[1]
+    rp, s = d["row_ptr"], d["senders"]
+    rows = np.arange(min(sample_nodes, N))
+    e_lo, e_hi = 0, int(rp[rows[-1] + 1])
+    Y = osh.real_sh(L, d["vec"][e_lo:e_hi].astype(np.float64))
+    x = d["x"].cpu().numpy()
+    w = d["w"][e_lo:e_hi].cpu().numpy()
+    prob = oc.Problem(L, L, L)
+    rp_sub = rp[:rows[-1] + 2]
+    s_sub = s[e_lo:e_hi]
+    nt = oc.max_threads()
+    t0 = time.perf_counter()
+    oc.fwd(prob, x, Y, w, rp_sub, s_sub, rows=rows)
+    t_fwd = time.perf_counter() - t0
+    t_bwd = 0.0
+    if fb:
+        G = d["grad_out"].cpu().numpy()
+        # the sampled edges grouped by sender (stable), as the backward walks them
+        recv = og.receivers_of(rp_sub)
+        order = np.argsort(s_sub, kind="stable")
+        send_ptr = np.zeros(N + 1, dtype=np.int64)
+        send_ptr[1:] = np.cumsum(np.bincount(s_sub, minlength=N))
+        senders_hit = np.unique(s_sub)
+        t0 = time.perf_counter()
+        oc.bwd_dx(prob, Y, w, G, send_ptr.astype(np.int32), order.astype(np.int32),
+                  recv[order].astype(np.int32), rows=senders_hit)
+        oc.bwd_edges(prob, x, Y, w, G, rp_sub, s_sub)
+        t_bwd = time.perf_counter() - t0
+    e_sample = e_hi - e_lo
+    t = t_fwd + t_bwd
+    step_bytes = fwd_bytes(*shp) + (bwd_bytes(*shp) if fb else 0)
+    edges_per_s = e_sample / t
+    gbs = edges_per_s * (step_bytes / E) / 1e9
+    what = "forward + backward (dx, dw, dY)" if fb else "forward"
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "edges_per_s": round(edges_per_s, 1), "seconds": round(t, 2),
+            "sample": f"{what} over the {e_sample} in-edges of the first {len(rows)} receivers "
+                      f"({e_sample / E:.1%} of the edges), fp64 C edge loop, {nt} OpenMP threads; "
+                      "GB/s scaled by the full step's bytes per edge"}
+
+
+# ------------------------------------------------------------ traffic from committed counters
+
+
+def committed_traffic(kernel_tag):
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != kernel_sources_sha():
+        return None        # kernels changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="l3fb", choices=sorted(WORKLOADS))
+    ap.add_argument("--channels", type=int, default=128, help="sweepC only")
+    ap.add_argument("--vec", action="store_true", help="l3fb with edge vectors instead of Y")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-nodes", type=int, default=2048)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the conv TP path here is "
+              "single-device and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tensor_product_message_amd as ctp
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
+    wl = WORKLOADS[args.workload](ctp, torch, dev, args)
+    timer = Timer(torch)
+    for _ in range(args.warmup):
+        wl["step"](timer)
+    torch.cuda.synchronize()
+    timer.reset()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    s0.record()
+    for _ in range(args.steps):
+        wl["step"](timer)
+    s1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = s0.elapsed_time(s1) / args.steps
+
+    value_kernels = wl.get("value_kernels", tuple(wl["kernel_bytes"]))
+    step_bytes = sum(wl["kernel_bytes"][k] for k in value_kernels)
+    if value_kernels != tuple(wl["kernel_bytes"]):
+        ms_value = sum(timer.mean_ms(k) for k in value_kernels)
+    else:
+        ms_value = ms_step
+    gbs = step_bytes / (ms_value * 1e-3) / 1e9
+    dom = wl["dominant"]
+    dom_ms = timer.mean_ms(dom)
+    dom_gbs = wl["kernel_bytes"][dom] / (dom_ms * 1e-3) / 1e9
+    kernels = {k: {"ms": round(timer.mean_ms(k), 4), "alg_bytes": wl["kernel_bytes"][k],
+                   "GB_s": round(wl["kernel_bytes"][k] / (timer.mean_ms(k) * 1e-3) / 1e9, 1),
+                   "pct_hbm_peak": round(100 * wl["kernel_bytes"][k] / (timer.mean_ms(k) * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 1)}
+               for k in wl["kernel_bytes"]}
+    traffic = committed_traffic(f"{args.workload}_{dom}")
+    line = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_value, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": wl["cfg"],
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+        "edges_per_s": round(wl["edges"] / (ms_value * 1e-3), 1),
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "wall_s": round(wall, 3), "kernel_sources_sha": kernel_sources_sha(),
+    }
+    if wl.get("cpu") and not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl["cpu"], args.cpu_sample_nodes)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * convtp.h - C ABI of the fused equivariant convolution tensor product
+ *            (MI355X / gfx950).
+ *
+ * The operation is the message-passing convolution of MACE-style interatomic
+ * potentials that the e3j paper (arXiv 2609.35099) accelerates: abstract
+ * ("message passing convolutions forward"), Table 1 (convolution throughput
+ * by channel count) and Table 2 (only the convolution block of MACE runs on
+ * the dedicated kernels).  For every edge e = j -> i:
+ *
+ *   out[i, l3 m3, c] = sum_e sum_{p = (l1,l2,l3)} w[e, p, c]
+ *                      sum_{m1,m2} C_p[m1][m2][m3] x[j, l1 m1, c] Y[e, l2 m2]
+ *
+ * with Y the real spherical harmonics of the edge direction and C_p the real
+ * Clebsch-Gordan coupling of path p.  Messages are never written to memory.
+ * The paths are all (l1,l2,l3) with l1 <= l_in, l2 <= l_sh, l3 <= l_out and
+ * |l1-l2| <= l3 <= l1+l2 (the admissible couplings of FlashCart, arXiv
+ * 2610.06409, section on spherical vs Cartesian products), in lexicographic
+ * order, and all paths with the same l3 are summed into one output block.
+ * The backward pass is the exact vector-Jacobian product (FlashCart, section
+ * on symbolic VJPs).
+ *
+ * Conventions.  Component index d(l, m) = l*l + l + m, m = -l..l; the l = 1
+ * block is proportional to (y, z, x).  Y is orthonormal on the sphere without
+ * the Condon-Shortley phase; C_p is orthonormal (sum over m1,m2 of
+ * C[m1,m2,m3] C[m1,m2,m3'] = delta) and, for odd l1+l2+l3, is the imaginary
+ * part of the complex CG transformed to the real basis (so path (1,1,1) maps
+ * Cartesian a, b to -(a x b)/sqrt 2).  A zero edge vector gives
+ * Y_00 = 1/sqrt(4 pi), every other Y = 0 and a zero vector gradient.
+ *
+ * Layout (all arrays contiguous, channel index fastest):
+ *   x[N][D_in][C], out[N][D_out][C], grad_out[N][D_out][C], dx[N][D_in][C]
+ *   w[E][P][C], dw[E][P][C]
+ *   Y[E][D_sh] (y_mode 0) or vec[E][3] (y_mode 1); dY / dvec alike
+ *   row_ptr[N+1], senders[E]: CSR by receiver (edges of receiver i are
+ *   row_ptr[i] .. row_ptr[i+1]-1); every edge array is in this CSR order.
+ *   send_ptr[N+1], send_perm[E], send_recv[E]: the same edges grouped by
+ *   sender, stable in CSR edge id (from conv_tp_build_transpose).
+ *   D_l = (l+1)^2, P = conv_tp_num_paths(...).
+ *
+ * Memory and ownership.  Array pointers are DEVICE pointers unless marked
+ * host.  The caller allocates and owns every buffer; the library never
+ * allocates, frees or retains caller memory.  It owns only a few bytes of
+ * per-device state for conv_tp_check_graph.  Outputs are overwritten, never
+ * accumulated into; rows with no edges get exact zeros.  Inputs and outputs
+ * must not overlap.
+ *
+ * Streams.  `stream` is a hipStream_t (0 = the null stream).  Every call
+ * except conv_tp_check_graph enqueues its kernels and returns without
+ * synchronising; kernel faults surface at the caller's next synchronisation.
+ *
+ * Errors.  Every argument check runs on the host before any HIP call, so an
+ * invalid call never touches the device.  Device contents (index ranges,
+ * monotone row pointers) are NOT checked on the hot path: out-of-range
+ * indices are undefined behaviour; conv_tp_check_graph validates a graph.
+ * On a non-zero status, conv_tp_last_error() returns a message (per thread).
+ *
+ * Determinism.  algo 0 (CSR forward) and the backward write each output
+ * element once, summing in a fixed order: results are bitwise reproducible.
+ * algo 1 (edge-parallel atomics) is not.
+ */
+#ifndef CONVTP_H
+#define CONVTP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    CTP_OK = 0,
+    CTP_EINVAL = 1,        /* null pointer, negative size, bad enum value */
+    CTP_EUNSUPPORTED = 2,  /* degree outside 0..3, unequal degrees, channels outside 1..1024,
+                              backward channel count above its limit, algo 1 in the backward */
+    CTP_EALIGN = 3,        /* a feature/weight array not 16-byte aligned, an index array not 4-byte aligned */
+    CTP_EHIP = 4,          /* HIP launch or runtime error (message from hipGetErrorString) */
+    CTP_EGRAPH = 5         /* graph arguments inconsistent (e.g. edges without nodes) */
+};
+
+typedef struct conv_tp_problem {
+    int32_t n_nodes;   /* N >= 0 */
+    int32_t n_edges;   /* E >= 0 */
+    int32_t channels;  /* C, 1..1024 */
+    int32_t l_in;      /* max degree of x, 0..3 */
+    int32_t l_sh;      /* max degree of Y, 0..3 */
+    int32_t l_out;     /* max degree of out, 0..3 (this build: l_in = l_sh = l_out) */
+    int32_t y_mode;    /* 0: Y[E][D_sh] given; 1: vec[E][3] given, Y evaluated in-kernel */
+    int32_t algo;      /* 0: CSR segmented sum, deterministic; 1: edge-parallel atomics (forward only) */
+} conv_tp_problem;
+
+/* Number of paths P for the degrees, or -1 (with a message) if a degree is
+ * outside 0..3.  Pure host function. */
+int32_t conv_tp_num_paths(int32_t l_in, int32_t l_sh, int32_t l_out);
+
+/* Path list: l123 (host, [P][3]) receives (l1, l2, l3) of every path in the
+ * order of w's second index.  Pure host function. */
+int32_t conv_tp_paths(int32_t l_in, int32_t l_sh, int32_t l_out, int32_t *l123);
+
+/* The library's real coupling tensor of path (l1, l2, l3) in double
+ * precision: out (host, [2l1+1][2l2+1][2l3+1]).  The kernels use these
+ * values rounded to fp32.  Pure host function; CTP_EINVAL if the triangle
+ * rule fails, CTP_EUNSUPPORTED for a degree above 3. */
+int32_t conv_tp_coupling(int32_t l1, int32_t l2, int32_t l3, double *out);
+
+/* Forward: out = conv(x, Y or vec, w) over the CSR graph.
+ * algo 0: one workgroup per receiver sums its edges in CSR order.
+ * algo 1: one workgroup per edge adds its message with fp32 atomics into
+ * out, which the call first zeroes. */
+int32_t conv_tp_fwd(const conv_tp_problem *prob, const float *x, const float *y_or_vec, const float *w,
+                    const int32_t *row_ptr, const int32_t *senders, float *out, void *stream);
+
+/* Backward for upstream gradient grad_out = dL/dout: writes dx, dw and dY
+ * (y_mode 0) or dvec = (dY/dvec)^T dY (y_mode 1).  One workgroup per sender
+ * walks its out-edges through (send_ptr, send_perm, send_recv).  algo must
+ * be 0; channels must fit one workgroup (C <= 512 when C % 128 == 0, else
+ * C <= 256). */
+int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y_or_vec,
+                    const float *w, const int32_t *row_ptr, const int32_t *senders, const int32_t *send_ptr,
+                    const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec,
+                    void *stream);
+
+/* Real spherical harmonics of edge vectors: Y[E][(l_sh+1)^2] from vec[E][3]. */
+int32_t conv_tp_sh(int32_t n_edges, int32_t l_sh, const float *vec, float *Y, void *stream);
+
+/* Vector gradient of the harmonics: dvec[e] = (dY/dvec)(vec_e)^T dY[e]. */
+int32_t conv_tp_sh_bwd(int32_t n_edges, int32_t l_sh, const float *vec, const float *dY, float *dvec,
+                       void *stream);
+
+/* Sender-sorted transpose of a CSR-by-receiver graph: send_ptr[N+1],
+ * send_perm[E] (CSR edge ids, ascending within each sender) and
+ * send_recv[E] (receiver of each).  Integer work, bit-exact and
+ * deterministic.  The graph must be valid (conv_tp_check_graph); for an
+ * invalid one the result is undefined but nothing outside the three output
+ * arrays is written. */
+int32_t conv_tp_build_transpose(int32_t n_nodes, int32_t n_edges, const int32_t *row_ptr, const int32_t *senders,
+                                int32_t *send_ptr, int32_t *send_perm, int32_t *send_recv, void *stream);
+
+/* Debug check of a CSR graph: *n_bad (host) receives the number of defects
+ * (row_ptr[0] != 0, each decreasing step of row_ptr, row_ptr[N] != E, each
+ * sender outside [0, N)).  Synchronises `stream`. */
+int32_t conv_tp_check_graph(int32_t n_nodes, int32_t n_edges, const int32_t *row_ptr, const int32_t *senders,
+                            int64_t *n_bad, void *stream);
+
+/* Message for the last non-zero status on this thread ("" if none). */
+const char *conv_tp_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int32_t conv_tp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVTP_H */

@@ -105,7 +105,10 @@ def _i32(a):
 
 
 def materialised_fwd(prob: Problem, x, Y, w, row_ptr, senders):
-    """out[N][D3][C]: every message built explicitly, then scatter-added."""
+    """out[N][D3][C]: every message built explicitly, then scatter-added.
+
+    einsum(optimize=True) only picks the pairwise contraction order of each
+    path's product; the arithmetic is the definition term by term."""
     x = np.asarray(x, dtype=np.float64)
     Y = np.asarray(Y, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
@@ -118,7 +121,7 @@ def materialised_fwd(prob: Problem, x, Y, w, row_ptr, senders):
         xs = x[senders, l1 * l1:(l1 + 1) ** 2, :]
         ys = Y[:, l2 * l2:(l2 + 1) ** 2]
         msg[:, l3 * l3:(l3 + 1) ** 2, :] += w[:, p, None, :] * np.einsum(
-            "abk,eac,eb->ekc", Cp, xs, ys)
+            "abk,eac,eb->ekc", Cp, xs, ys, optimize=True)
     out = np.zeros((n, prob.D3, c))
     np.add.at(out, recv, msg)
     return out
@@ -142,9 +145,10 @@ def materialised_bwd(prob: Problem, x, Y, w, G, row_ptr, senders):
         s2 = slice(l2 * l2, (l2 + 1) ** 2)
         s3 = slice(l3 * l3, (l3 + 1) ** 2)
         xs, ys, gs = x[senders, s1, :], Y[:, s2], gd[:, s3, :]
-        dx_e[:, s1, :] += w[:, p, None, :] * np.einsum("abk,eb,ekc->eac", Cp, ys, gs)
-        dw[:, p, :] = np.einsum("abk,eac,eb,ekc->ec", Cp, xs, ys, gs)
-        dY[:, s2] += np.einsum("abk,ec,eac,ekc->eb", Cp, w[:, p, :], xs, gs)
+        dx_e[:, s1, :] += w[:, p, None, :] * np.einsum("abk,eb,ekc->eac", Cp, ys, gs, optimize=True)
+        dw[:, p, :] = np.einsum("abk,eac,eb,ekc->ec", Cp, xs, ys, gs, optimize=True)
+        dY[:, s2] += np.einsum("abk,ec,eac,ekc->eb", Cp, w[:, p, :], xs, gs,
+                                 optimize=True)
     dx = np.zeros((n, prob.D1, c))
     np.add.at(dx, senders, dx_e)
     return dx, dw, dY

@@ -1,0 +1,281 @@
+// C ABI front: argument validation (host only, before any HIP call), error
+// reporting, path/coupling queries and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "../../include/convtp.h"
+#include "kernels.hpp"
+#include "tables.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return CTP_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(CTP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// A pointer is required when its array has elements; alignment is checked
+// whenever it is non-null.
+int need(const void* p, int64_t count, uintptr_t align, const char* name) {
+    if (count > 0 && p == nullptr) return fail(CTP_EINVAL, "%s is null but has %lld elements", name, (long long)count);
+    if (p != nullptr && !aligned(p, align))
+        return fail(CTP_EALIGN, "%s is not %u-byte aligned", name, (unsigned)align);
+    return CTP_OK;
+}
+
+int check_degree(int l, const char* name) {
+    if (l < 0 || l > ctp::kMaxL) return fail(CTP_EUNSUPPORTED, "%s = %d outside 0..%d", name, l, ctp::kMaxL);
+    return CTP_OK;
+}
+
+struct Shape {
+    int64_t N, E, C, D1, D2, D3, P, S;
+};
+
+int check_problem(const conv_tp_problem* pr, Shape* s) {
+    if (pr == nullptr) return fail(CTP_EINVAL, "problem is null");
+    if (pr->n_nodes < 0 || pr->n_edges < 0) return fail(CTP_EINVAL, "negative node or edge count");
+    if (pr->channels < 1) return fail(CTP_EINVAL, "channels = %d must be >= 1", pr->channels);
+    if (pr->channels > 1024) return fail(CTP_EUNSUPPORTED, "channels = %d above 1024", pr->channels);
+    if (int r = check_degree(pr->l_in, "l_in")) return r;
+    if (int r = check_degree(pr->l_sh, "l_sh")) return r;
+    if (int r = check_degree(pr->l_out, "l_out")) return r;
+    if (pr->l_in != pr->l_sh || pr->l_sh != pr->l_out)
+        return fail(CTP_EUNSUPPORTED, "degrees (%d,%d,%d) must be equal in this build", pr->l_in, pr->l_sh, pr->l_out);
+    if (pr->y_mode != 0 && pr->y_mode != 1) return fail(CTP_EINVAL, "y_mode = %d not 0 or 1", pr->y_mode);
+    if (pr->algo != 0 && pr->algo != 1) return fail(CTP_EINVAL, "algo = %d not 0 or 1", pr->algo);
+    if (pr->n_nodes == 0 && pr->n_edges > 0) return fail(CTP_EGRAPH, "edges without nodes");
+    s->N = pr->n_nodes;
+    s->E = pr->n_edges;
+    s->C = pr->channels;
+    s->D1 = ctp::dim_of(pr->l_in);
+    s->D2 = ctp::dim_of(pr->l_sh);
+    s->D3 = ctp::dim_of(pr->l_out);
+    s->P = ctp::num_paths(pr->l_in, pr->l_sh, pr->l_out);
+    s->S = pr->y_mode ? 3 : s->D2;
+    return CTP_OK;
+}
+
+ctp::LaunchArgs base_args(const conv_tp_problem* pr) {
+    ctp::LaunchArgs a{};
+    a.L = pr->l_in;
+    a.n_nodes = pr->n_nodes;
+    a.n_edges = pr->n_edges;
+    a.C = pr->channels;
+    a.algo = pr->algo;
+    a.vec_mode = pr->y_mode;
+    return a;
+}
+
+std::mutex g_bad_mu;
+std::unordered_map<int, unsigned long long*> g_bad_buf;   // per-device counter for conv_tp_check_graph
+
+}  // namespace
+
+namespace ctp {
+
+int host_num_paths(int l1, int l2, int l3) { return num_paths(l1, l2, l3); }
+
+int host_paths(int l_in, int l_sh, int l_out, int32_t* l123) {
+    int n = 0;
+    for (int a = 0; a <= l_in; ++a)
+        for (int b = 0; b <= l_sh; ++b)
+            for (int c = 0; c <= l_out; ++c)
+                if (triangle(a, b, c)) {
+                    l123[3 * n] = a;
+                    l123[3 * n + 1] = b;
+                    l123[3 * n + 2] = c;
+                    ++n;
+                }
+    return n;
+}
+
+int host_coupling(int l1, int l2, int l3, double* out) {
+    const int n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+    for (int a = 0; a < 2 * l1 + 1; ++a)
+        for (int b = 0; b < n2; ++b)
+            for (int c = 0; c < n3; ++c)
+                out[(a * n2 + b) * n3 + c] = real_coupling(l1, l2, l3, a - l1, b - l2, c - l3);
+    return 0;
+}
+
+}  // namespace ctp
+
+extern "C" {
+
+int32_t conv_tp_version(void) { return 100; }
+
+const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
+
+int32_t conv_tp_num_paths(int32_t l_in, int32_t l_sh, int32_t l_out) {
+    if (check_degree(l_in, "l_in") || check_degree(l_sh, "l_sh") || check_degree(l_out, "l_out")) return -1;
+    ok();
+    return ctp::host_num_paths(l_in, l_sh, l_out);
+}
+
+int32_t conv_tp_paths(int32_t l_in, int32_t l_sh, int32_t l_out, int32_t* l123) {
+    if (int r = check_degree(l_in, "l_in")) return r;
+    if (int r = check_degree(l_sh, "l_sh")) return r;
+    if (int r = check_degree(l_out, "l_out")) return r;
+    if (l123 == nullptr) return fail(CTP_EINVAL, "l123 is null");
+    ctp::host_paths(l_in, l_sh, l_out, l123);
+    return ok();
+}
+
+int32_t conv_tp_coupling(int32_t l1, int32_t l2, int32_t l3, double* out) {
+    if (int r = check_degree(l1, "l1")) return r;
+    if (int r = check_degree(l2, "l2")) return r;
+    if (int r = check_degree(l3, "l3")) return r;
+    if (!ctp::triangle(l1, l2, l3)) return fail(CTP_EINVAL, "path (%d,%d,%d) violates the triangle rule", l1, l2, l3);
+    if (out == nullptr) return fail(CTP_EINVAL, "out is null");
+    ctp::host_coupling(l1, l2, l3, out);
+    return ok();
+}
+
+int32_t conv_tp_fwd(const conv_tp_problem* prob, const float* x, const float* y_or_vec, const float* w,
+                    const int32_t* row_ptr, const int32_t* senders, float* out, void* stream) {
+    Shape s{};
+    if (int r = check_problem(prob, &s)) return r;
+    if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
+    if (int r = need(y_or_vec, s.E * s.S, 4, "y_or_vec")) return r;
+    if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;
+    if (int r = need(row_ptr, s.N + 1, 4, "row_ptr")) return r;
+    if (int r = need(senders, s.E, 4, "senders")) return r;
+    if (int r = need(out, s.N * s.D3 * s.C, 16, "out")) return r;
+    ctp::LaunchArgs a = base_args(prob);
+    a.x = x;
+    a.y = y_or_vec;
+    a.w = w;
+    a.row_ptr = row_ptr;
+    a.senders = senders;
+    a.out = out;
+    return hip_status(ctp::launch_fwd(a, static_cast<hipStream_t>(stream)), "conv_tp_fwd launch");
+}
+
+int32_t conv_tp_bwd(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* y_or_vec,
+                    const float* w, const int32_t* row_ptr, const int32_t* senders, const int32_t* send_ptr,
+                    const int32_t* send_perm, const int32_t* send_recv, float* dx, float* dw, float* dy_or_dvec,
+                    void* stream) {
+    Shape s{};
+    if (int r = check_problem(prob, &s)) return r;
+    if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the backward has only the deterministic algorithm (algo 0)");
+    if (!ctp::bwd_supports_channels(prob->channels))
+        return fail(CTP_EUNSUPPORTED, "backward needs C <= 512 (C %% 128 == 0) or C <= 256, got %d", prob->channels);
+    if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
+    if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
+    if (int r = need(y_or_vec, s.E * s.S, 4, "y_or_vec")) return r;
+    if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;
+    if (int r = need(row_ptr, s.N + 1, 4, "row_ptr")) return r;
+    if (int r = need(senders, s.E, 4, "senders")) return r;
+    if (int r = need(send_ptr, s.N + 1, 4, "send_ptr")) return r;
+    if (int r = need(send_perm, s.E, 4, "send_perm")) return r;
+    if (int r = need(send_recv, s.E, 4, "send_recv")) return r;
+    if (int r = need(dx, s.N * s.D1 * s.C, 16, "dx")) return r;
+    if (int r = need(dw, s.E * s.P * s.C, 16, "dw")) return r;
+    if (int r = need(dy_or_dvec, s.E * s.S, 4, "dy_or_dvec")) return r;
+    ctp::LaunchArgs a = base_args(prob);
+    a.grad = grad_out;
+    a.x = x;
+    a.y = y_or_vec;
+    a.w = w;
+    a.row_ptr = row_ptr;
+    a.senders = senders;
+    a.send_ptr = send_ptr;
+    a.send_perm = send_perm;
+    a.send_recv = send_recv;
+    a.dx = dx;
+    a.dw = dw;
+    a.dy = dy_or_dvec;
+    return hip_status(ctp::launch_bwd(a, static_cast<hipStream_t>(stream)), "conv_tp_bwd launch");
+}
+
+int32_t conv_tp_sh(int32_t n_edges, int32_t l_sh, const float* vec, float* Y, void* stream) {
+    if (n_edges < 0) return fail(CTP_EINVAL, "negative edge count");
+    if (int r = check_degree(l_sh, "l_sh")) return r;
+    if (int r = need(vec, (int64_t)n_edges * 3, 4, "vec")) return r;
+    if (int r = need(Y, (int64_t)n_edges * ctp::dim_of(l_sh), 4, "Y")) return r;
+    return hip_status(ctp::launch_sh(l_sh, n_edges, vec, Y, static_cast<hipStream_t>(stream)), "conv_tp_sh launch");
+}
+
+int32_t conv_tp_sh_bwd(int32_t n_edges, int32_t l_sh, const float* vec, const float* dY, float* dvec,
+                       void* stream) {
+    if (n_edges < 0) return fail(CTP_EINVAL, "negative edge count");
+    if (int r = check_degree(l_sh, "l_sh")) return r;
+    if (int r = need(vec, (int64_t)n_edges * 3, 4, "vec")) return r;
+    if (int r = need(dY, (int64_t)n_edges * ctp::dim_of(l_sh), 4, "dY")) return r;
+    if (int r = need(dvec, (int64_t)n_edges * 3, 4, "dvec")) return r;
+    return hip_status(ctp::launch_sh_bwd(l_sh, n_edges, vec, dY, dvec, static_cast<hipStream_t>(stream)),
+                      "conv_tp_sh_bwd launch");
+}
+
+int32_t conv_tp_build_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* row_ptr, const int32_t* senders,
+                                int32_t* send_ptr, int32_t* send_perm, int32_t* send_recv, void* stream) {
+    if (n_nodes < 0 || n_edges < 0) return fail(CTP_EINVAL, "negative node or edge count");
+    if (n_nodes == 0 && n_edges > 0) return fail(CTP_EGRAPH, "edges without nodes");
+    if (int r = need(row_ptr, (int64_t)n_nodes + 1, 4, "row_ptr")) return r;
+    if (int r = need(senders, n_edges, 4, "senders")) return r;
+    if (int r = need(send_ptr, (int64_t)n_nodes + 1, 4, "send_ptr")) return r;
+    if (int r = need(send_perm, n_edges, 4, "send_perm")) return r;
+    if (int r = need(send_recv, n_edges, 4, "send_recv")) return r;
+    return hip_status(ctp::launch_transpose(n_nodes, n_edges, row_ptr, senders, send_ptr, send_perm, send_recv,
+                                            static_cast<hipStream_t>(stream)),
+                      "conv_tp_build_transpose launch");
+}
+
+int32_t conv_tp_check_graph(int32_t n_nodes, int32_t n_edges, const int32_t* row_ptr, const int32_t* senders,
+                            int64_t* n_bad, void* stream) {
+    if (n_nodes < 0 || n_edges < 0) return fail(CTP_EINVAL, "negative node or edge count");
+    if (int r = need(row_ptr, (int64_t)n_nodes + 1, 4, "row_ptr")) return r;
+    if (int r = need(senders, n_edges, 4, "senders")) return r;
+    if (n_bad == nullptr) return fail(CTP_EINVAL, "n_bad is null");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e, "hipGetDevice");
+    // one counter per device; the lock also serialises concurrent checks that share it
+    std::lock_guard<std::mutex> lk(g_bad_mu);
+    unsigned long long* d_bad = nullptr;
+    auto it = g_bad_buf.find(dev);
+    if (it == g_bad_buf.end()) {
+        if (hipError_t e = hipMalloc(&d_bad, sizeof(unsigned long long)); e != hipSuccess)
+            return hip_status(e, "hipMalloc(check counter)");
+        g_bad_buf[dev] = d_bad;
+    } else {
+        d_bad = it->second;
+    }
+    unsigned long long h_bad = 0;
+    if (hipError_t e = hipMemsetAsync(d_bad, 0, sizeof(h_bad), st); e != hipSuccess) return hip_status(e, "memset");
+    if (hipError_t e = ctp::launch_check_graph(n_nodes, n_edges, row_ptr, senders, d_bad, st); e != hipSuccess)
+        return hip_status(e, "conv_tp_check_graph launch");
+    if (hipError_t e = hipMemcpyAsync(&h_bad, d_bad, sizeof(h_bad), hipMemcpyDeviceToHost, st); e != hipSuccess)
+        return hip_status(e, "copy");
+    if (hipError_t e = hipStreamSynchronize(st); e != hipSuccess) return hip_status(e, "synchronize");
+    *n_bad = static_cast<int64_t>(h_bad);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,588 @@
+// HIP kernels of the fused equivariant convolution tensor product (gfx950).
+//
+// Operation (e3j, arXiv 2609.35099, abstract and Table 1: message-passing
+// convolution without materialised messages; FlashCart, arXiv 2610.06409,
+// receiver-sorted convolution and its VJP):
+//
+//   out[i, l3 m3, c] = sum_{e = j->i} sum_{p: l3_p = l3} w[e,p,c]
+//                      sum_{m1} T_{p,e}[m1][m3] x[j, l1 m1, c],
+//   T_{p,e}[m1][m3]  = sum_{m2} C_p[m1][m2][m3] Y[e, l2 m2].
+//
+// Layout: x[N][D1][C], out[N][D3][C], w[E][P][C] (channel fastest, so every
+// wave-wide access is a contiguous run of C floats), Y[E][D2] or vec[E][3];
+// edges in CSR-by-receiver order.
+//
+// Mapping: one workgroup per receiver (forward) or sender (backward) and per
+// channel tile; lane <-> channel (CPL = 1 or 2 adjacent channels per lane).
+// Per edge, T_{p,e} is shared by every channel: the workgroup builds it once
+// in LDS (lane-parallel, <= 2 terms per entry) and every lane then reads it by
+// broadcast.  The path loops are unrolled at compile time over the constexpr
+// tables, so each coupling coefficient is an instruction constant and every
+// partial sum lives in registers.
+//
+// Determinism: the CSR forward and the sender-sorted backward write every
+// output element exactly once, summing edges and paths in a fixed order (no
+// atomics).  The edge-parallel atomic forward exists only as a comparison.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ctp {
+
+__constant__ SlotTab<0> kSlot0 = make_slot_tab<0>();
+__constant__ SlotTab<1> kSlot1 = make_slot_tab<1>();
+__constant__ SlotTab<2> kSlot2 = make_slot_tab<2>();
+__constant__ SlotTab<3> kSlot3 = make_slot_tab<3>();
+__constant__ ShTab kShTab = make_sh_tab();
+
+template <> __device__ __forceinline__ const SlotDev* slot_tab<0>() { return kSlot0.s; }
+template <> __device__ __forceinline__ const SlotDev* slot_tab<1>() { return kSlot1.s; }
+template <> __device__ __forceinline__ const SlotDev* slot_tab<2>() { return kSlot2.s; }
+template <> __device__ __forceinline__ const SlotDev* slot_tab<3>() { return kSlot3.s; }
+__device__ __forceinline__ const ShTab& sh_tab() { return kShTab; }
+
+constexpr int kMaxThreads = 256;
+
+// ------------------------------------------------------------ per-edge building blocks
+
+// Y of edge e into sY (lanes < D2): read (Y mode) or evaluated from vec.
+template <int D2, bool VEC>
+__device__ __forceinline__ void stage_sh(float* sY, const float* __restrict__ yv, long e, int tid) {
+    if (tid < D2) {
+        if constexpr (VEC) {
+            const float* v = yv + 3 * e;
+            sY[tid] = sh_component(tid, v[0], v[1], v[2]);
+        } else {
+            sY[tid] = yv[e * D2 + tid];
+        }
+    }
+}
+
+// T_{p,e} for all paths into sT, lane-parallel over the slots.
+template <int L>
+__device__ __forceinline__ void build_T(float* sT, const float* sY, int tid, int nth) {
+    constexpr int NT = Spec<L, L, L>::NT;
+    const SlotDev* tab = slot_tab<L>();
+    for (int t = tid; t < NT; t += nth) {
+        const SlotDev s = tab[t];
+        sT[t] = s.c1 * sY[s.yy & 0xff] + s.c2 * sY[s.yy >> 8];
+    }
+}
+
+// acc[l3 m3] += sum_p w_p * (T_p^T x[l1])[m3] for one edge and CPL channels.
+template <class S, int CPL>
+__device__ __forceinline__ void edge_forward(float (&acc)[S::D3][CPL], const float (&xv)[S::D1][CPL],
+                                             const float (&wv)[S::P][CPL], const float* sT) {
+    static_for<S::P>([&](auto pI) __attribute__((always_inline)) {
+        constexpr int p = decltype(pI)::value;
+        constexpr PathL q = S::paths[p];
+        constexpr int n1 = 2 * q.l1 + 1, n3 = 2 * q.l3 + 1;
+        constexpr int o1 = q.l1 * q.l1, o3 = q.l3 * q.l3;
+        constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
+        if constexpr (n1 <= n3) {
+            // scale x by w first: n1 products, then one FMA per slot
+            float xs[n1][CPL];
+#pragma unroll
+            for (int a = 0; a < n1; ++a)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) xs[a][c] = wv[p][c] * xv[o1 + a][c];
+            static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
+                constexpr int t = t0 + decltype(tI)::value;
+                constexpr TSlot s = S::slots[t];
+                const float tv = sT[t];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    acc[o3 + s.m3][c] = __builtin_fmaf(tv, xs[s.m1][c], acc[o3 + s.m3][c]);
+            });
+        } else {
+            // contract T with x first: one FMA per slot, then n3 FMAs with w
+            float u[n3][CPL];
+            static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
+                constexpr int t = t0 + decltype(tI)::value;
+                constexpr TSlot s = S::slots[t];
+                const float tv = sT[t];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    if constexpr (first_m3<S>(t))
+                        u[s.m3][c] = tv * xv[o1 + s.m1][c];
+                    else
+                        u[s.m3][c] = __builtin_fmaf(tv, xv[o1 + s.m1][c], u[s.m3][c]);
+                }
+            });
+#pragma unroll
+            for (int k = 0; k < n3; ++k)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[o3 + k][c] = __builtin_fmaf(wv[p][c], u[k][c], acc[o3 + k][c]);
+        }
+    });
+}
+
+template <class S, int CPL>
+__device__ __forceinline__ void load_edge_operands(float (&xv)[S::D1][CPL], float (&wv)[S::P][CPL],
+                                                   const float* __restrict__ x, const float* __restrict__ w,
+                                                   long j, long e, int C, int c) {
+    const float* xr = x + j * S::D1 * C + c;
+    const float* wr = w + e * S::P * C + c;
+#pragma unroll
+    for (int d = 0; d < S::D1; ++d) load_ch<CPL>(xr + (long)d * C, xv[d]);
+#pragma unroll
+    for (int p = 0; p < S::P; ++p) load_ch<CPL>(wr + (long)p * C, wv[p]);
+}
+
+// ------------------------------------------------------------ K1: CSR forward (deterministic)
+
+template <int L, int CPL, bool VEC>
+__global__ void __launch_bounds__(kMaxThreads)
+k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, const float* __restrict__ w,
+          const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ out) {
+    using S = Spec<L, L, L>;
+    constexpr int D2 = S::D2, D3 = S::D3, NTP = (S::NT + 3) & ~3;
+    __shared__ float sT[2][NTP];
+    __shared__ float sY[2][16];
+
+    const int i = blockIdx.x;
+    const int tid = threadIdx.x, nth = blockDim.x;
+    const int c0 = (blockIdx.y * nth + tid) * CPL;
+    const bool active = c0 < C;
+    const int cl = active ? c0 : 0;
+
+    float acc[D3][CPL];
+#pragma unroll
+    for (int d = 0; d < D3; ++d)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[d][c] = 0.0f;
+
+    const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
+    for (int e = e0; e < e1; ++e) {
+        const int buf = (e - e0) & 1;
+        float xv[S::D1][CPL], wv[S::P][CPL];
+        load_edge_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, cl);
+        stage_sh<D2, VEC>(sY[buf], yv, e, tid);
+        __syncthreads();
+        build_T<L>(sT[buf], sY[buf], tid, nth);
+        __syncthreads();
+        edge_forward<S, CPL>(acc, xv, wv, sT[buf]);
+    }
+    if (active) {
+        float* o = out + (long)i * D3 * C + c0;
+#pragma unroll
+        for (int d = 0; d < D3; ++d) store_ch<CPL>(o + (long)d * C, acc[d]);
+    }
+}
+
+// ------------------------------------------------------------ K2: edge-parallel atomic forward (comparison)
+
+__global__ void k_zero(float* __restrict__ p, long n) {
+    long k = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (; k < n; k += stride) p[k] = 0.0f;
+}
+
+template <int L, int CPL, bool VEC>
+__global__ void __launch_bounds__(kMaxThreads)
+k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __restrict__ yv,
+             const float* __restrict__ w, const int* __restrict__ row_ptr, const int* __restrict__ senders,
+             float* __restrict__ out) {
+    using S = Spec<L, L, L>;
+    constexpr int D2 = S::D2, D3 = S::D3, NTP = (S::NT + 3) & ~3;
+    __shared__ float sT[NTP];
+    __shared__ float sY[16];
+
+    const long e = blockIdx.x;
+    const int tid = threadIdx.x, nth = blockDim.x;
+    const int c0 = (blockIdx.y * nth + tid) * CPL;
+    const bool active = c0 < C;
+    const int cl = active ? c0 : 0;
+
+    // receiver of edge e: last i with row_ptr[i] <= e
+    int lo = 0, hi = n_nodes;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (row_ptr[mid] <= e) lo = mid; else hi = mid;
+    }
+    const int i = lo;
+
+    float xv[S::D1][CPL], wv[S::P][CPL];
+    load_edge_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, cl);
+    stage_sh<D2, VEC>(sY, yv, e, tid);
+    __syncthreads();
+    build_T<L>(sT, sY, tid, nth);
+    __syncthreads();
+    float acc[D3][CPL];
+#pragma unroll
+    for (int d = 0; d < D3; ++d)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[d][c] = 0.0f;
+    edge_forward<S, CPL>(acc, xv, wv, sT);
+    if (active) {
+        float* o = out + (long)i * D3 * C + c0;
+#pragma unroll
+        for (int d = 0; d < D3; ++d)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + c, acc[d][c]);
+    }
+}
+
+// ------------------------------------------------------------ K3: sender-sorted backward (deterministic)
+//
+// For sender j and each out-edge e = j -> i (sender-sorted, stable in CSR id):
+//   v_p[m1]      = sum_m3 T_p[m1][m3] G[i, l3 m3]
+//   dw[e,p]      = sum_m1 x[j, l1 m1] v_p[m1]
+//   dx[j, l1 m1] += w_p v_p[m1]                      (registers; stored once)
+//   B_p[m2]      = sum_{m1,m3} C_p[m1][m2][m3] x[j, l1 m1] G[i, l3 m3]
+//   dY[e, l2 m2] = sum_c sum_p w_p B_p[m2]           (lanes, then waves, fixed order)
+// With VEC, dvec[e] = J(vec_e)^T dY[e] instead of dY.
+
+template <int L, int CPL, bool VEC>
+__global__ void __launch_bounds__(kMaxThreads)
+k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ yv,
+             const float* __restrict__ w, const int* __restrict__ send_ptr, const int* __restrict__ send_perm,
+             const int* __restrict__ send_recv, float* __restrict__ dx, float* __restrict__ dw,
+             float* __restrict__ dyv) {
+    using S = Spec<L, L, L>;
+    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NTP = (S::NT + 3) & ~3;
+    __shared__ float sT[2][NTP];
+    __shared__ float sY[2][16];
+    __shared__ float sRed[2][kMaxThreads / 64][16];
+
+    const int j = blockIdx.x;
+    const int tid = threadIdx.x, nth = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6, nwaves = nth >> 6;
+    const int c0 = tid * CPL;
+    const bool active = c0 < C;
+    const int cl = active ? c0 : 0;
+
+    float xv[D1][CPL], dxa[D1][CPL];
+    {
+        const float* xr = x + (long)j * D1 * C + cl;
+#pragma unroll
+        for (int d = 0; d < D1; ++d) {
+            load_ch<CPL>(xr + (long)d * C, xv[d]);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                xv[d][c] = active ? xv[d][c] : 0.0f;
+                dxa[d][c] = 0.0f;
+            }
+        }
+    }
+
+    const int k0 = send_ptr[j], k1 = send_ptr[j + 1];
+    for (int k = k0; k < k1; ++k) {
+        const int buf = (k - k0) & 1;
+        const long e = send_perm[k];
+        const long i = send_recv[k];
+        float gv[D3][CPL], wv[P][CPL];
+        {
+            const float* gr = G + i * D3 * C + cl;
+            const float* wr = w + e * P * C + cl;
+#pragma unroll
+            for (int d = 0; d < D3; ++d) load_ch<CPL>(gr + (long)d * C, gv[d]);
+#pragma unroll
+            for (int p = 0; p < P; ++p) load_ch<CPL>(wr + (long)p * C, wv[p]);
+        }
+        stage_sh<D2, VEC>(sY[buf], yv, e, tid);
+        __syncthreads();
+        build_T<L>(sT[buf], sY[buf], tid, nth);
+        __syncthreads();
+        const float* T = sT[buf];
+
+        // dx and dw through v_p = T_p^T g
+        float* dwr = dw + e * P * C + c0;
+        static_for<P>([&](auto pI) __attribute__((always_inline)) {
+            constexpr int p = decltype(pI)::value;
+            constexpr PathL q = S::paths[p];
+            constexpr int n1 = 2 * q.l1 + 1;
+            constexpr int o1 = q.l1 * q.l1, o3 = q.l3 * q.l3;
+            constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
+            float v[n1][CPL];
+            static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
+                constexpr int t = t0 + decltype(tI)::value;
+                constexpr TSlot s = S::slots[t];
+                const float tv = T[t];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    if constexpr (first_m1<S>(t))
+                        v[s.m1][c] = tv * gv[o3 + s.m3][c];
+                    else
+                        v[s.m1][c] = __builtin_fmaf(tv, gv[o3 + s.m3][c], v[s.m1][c]);
+                }
+            });
+            float dwv[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                dwv[c] = xv[o1][c] * v[0][c];
+#pragma unroll
+                for (int a = 1; a < n1; ++a) dwv[c] = __builtin_fmaf(xv[o1 + a][c], v[a][c], dwv[c]);
+            }
+            if (active) store_ch<CPL>(dwr + (long)p * C, dwv);
+#pragma unroll
+            for (int a = 0; a < n1; ++a)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) dxa[o1 + a][c] = __builtin_fmaf(wv[p][c], v[a][c], dxa[o1 + a][c]);
+        });
+
+        // dY: per-lane partial sums over this lane's channels, path by path
+        float dya[D2];
+#pragma unroll
+        for (int d = 0; d < D2; ++d) dya[d] = 0.0f;
+        static_for<L + 1>([&](auto l1I) __attribute__((always_inline)) {
+            constexpr int l1 = decltype(l1I)::value;
+            static_for<L + 1>([&](auto l3I) __attribute__((always_inline)) {
+                constexpr int l3 = decltype(l3I)::value;
+                constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
+                float xg[n1][n3][CPL];
+#pragma unroll
+                for (int a = 0; a < n1; ++a)
+#pragma unroll
+                    for (int b = 0; b < n3; ++b)
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) xg[a][b][c] = xv[l1 * l1 + a][c] * gv[l3 * l3 + b][c];
+                static_for<P>([&](auto pI) __attribute__((always_inline)) {
+                    constexpr int p = decltype(pI)::value;
+                    constexpr PathL q = S::paths[p];
+                    if constexpr (q.l1 == l1 && q.l3 == l3) {
+                        constexpr int n2 = 2 * q.l2 + 1, o2 = q.l2 * q.l2;
+                        constexpr int z0 = nz_begin<S>(p), z1 = nz_begin<S>(p + 1);
+                        float B[n2][CPL];
+                        static_for<z1 - z0>([&](auto zI) __attribute__((always_inline)) {
+                            constexpr int n = z0 + decltype(zI)::value;
+                            constexpr CgNz nzv = S::nz[n];
+#pragma unroll
+                            for (int c = 0; c < CPL; ++c) {
+                                if constexpr (nz_first_m2<S>(n))
+                                    B[nzv.m2][c] = nzv.c * xg[nzv.m1][nzv.m3][c];
+                                else
+                                    B[nzv.m2][c] = __builtin_fmaf(nzv.c, xg[nzv.m1][nzv.m3][c], B[nzv.m2][c]);
+                            }
+                        });
+#pragma unroll
+                        for (int b = 0; b < n2; ++b)
+#pragma unroll
+                            for (int c = 0; c < CPL; ++c) dya[o2 + b] = __builtin_fmaf(wv[p][c], B[b][c], dya[o2 + b]);
+                    }
+                });
+            });
+        });
+
+        // reduce over lanes (DPP, fixed order), then over waves (LDS, fixed order)
+        float tot = 0.0f;
+#pragma unroll
+        for (int d = 0; d < D2; ++d) {
+            const float r = lane_value(wave_sum_to_last(dya[d]), 63);
+            tot = (lane == d) ? r : tot;
+        }
+        if (nwaves > 1) {
+            if (lane < D2) sRed[buf][wave][lane] = tot;
+            __syncthreads();
+            if (tid < D2) {
+                float s = sRed[buf][0][tid];
+                for (int q = 1; q < nwaves; ++q) s += sRed[buf][q][tid];
+                tot = s;
+            }
+        }
+        if constexpr (VEC) {
+            // dvec = (I - r r^T)/|v| * sum_k dY_k grad Y_k(r), lanes < D2 of wave 0
+            if (wave == 0) {
+                const float* vp = yv + 3 * e;
+                const float vx = vp[0], vy = vp[1], vz = vp[2];
+                const float n2 = vx * vx + vy * vy + vz * vz;
+                const float inv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+                const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
+                float g[3] = {0.0f, 0.0f, 0.0f};
+                if (lane < D2) {
+                    sh_component_grad(lane, rx, ry, rz, g);
+                    g[0] *= tot; g[1] *= tot; g[2] *= tot;
+                }
+                const float gx = lane_value(wave_sum_to_last(g[0]), 63);
+                const float gy = lane_value(wave_sum_to_last(g[1]), 63);
+                const float gz = lane_value(wave_sum_to_last(g[2]), 63);
+                const float rg = rx * gx + ry * gy + rz * gz;
+                if (lane < 3) {
+                    const float gl = lane == 0 ? gx : (lane == 1 ? gy : gz);
+                    const float rl = lane == 0 ? rx : (lane == 1 ? ry : rz);
+                    dyv[3 * e + lane] = (gl - rg * rl) * inv;
+                }
+            }
+        } else {
+            if (tid < D2) dyv[e * D2 + tid] = tot;
+        }
+    }
+
+    if (active) {
+        float* o = dx + (long)j * D1 * C + c0;
+#pragma unroll
+        for (int d = 0; d < D1; ++d) store_ch<CPL>(o + (long)d * C, dxa[d]);
+    }
+}
+
+// ------------------------------------------------------------ standalone harmonics (vec -> Y, dY -> dvec)
+
+template <int L>
+__global__ void k_sh(long n_edges, const float* __restrict__ vec, float* __restrict__ Y) {
+    constexpr int D = (L + 1) * (L + 1);
+    const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_edges * D) return;
+    const long e = t / D;
+    const int k = static_cast<int>(t - e * D);
+    Y[t] = sh_component(k, vec[3 * e], vec[3 * e + 1], vec[3 * e + 2]);
+}
+
+template <int L>
+__global__ void k_sh_bwd(long n_edges, const float* __restrict__ vec, const float* __restrict__ dY,
+                         float* __restrict__ dvec) {
+    constexpr int D = (L + 1) * (L + 1);
+    const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n_edges) return;
+    const float vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    const float n2 = vx * vx + vy * vy + vz * vz;
+    if (n2 == 0.0f) {
+        dvec[3 * e] = dvec[3 * e + 1] = dvec[3 * e + 2] = 0.0f;
+        return;
+    }
+    const float inv = 1.0f / sqrtf(n2);
+    const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
+    float gx = 0.0f, gy = 0.0f, gz = 0.0f;
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        float g[3];
+        sh_component_grad(k, rx, ry, rz, g);
+        const float d = dY[e * D + k];
+        gx = __builtin_fmaf(d, g[0], gx);
+        gy = __builtin_fmaf(d, g[1], gy);
+        gz = __builtin_fmaf(d, g[2], gz);
+    }
+    const float rg = rx * gx + ry * gy + rz * gz;
+    dvec[3 * e] = (gx - rg * rx) * inv;
+    dvec[3 * e + 1] = (gy - rg * ry) * inv;
+    dvec[3 * e + 2] = (gz - rg * rz) * inv;
+}
+
+// ------------------------------------------------------------ launchers
+
+namespace {
+
+struct ChanMap {
+    int cpl, waves, tiles;   // channels per lane, waves per workgroup, channel tiles (grid.y)
+};
+
+ChanMap chan_map(int C, int max_waves) {
+    ChanMap m{};
+    m.cpl = (C % 128 == 0) ? 2 : 1;
+    const int per_wave = 64 * m.cpl;
+    const int need = (C + per_wave - 1) / per_wave;
+    m.waves = need < max_waves ? need : max_waves;
+    m.tiles = (need + m.waves - 1) / m.waves;
+    return m;
+}
+
+template <int L, int CPL>
+hipError_t fwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
+    dim3 block(64 * m.waves);
+    if (a.algo == 0) {
+        dim3 grid(a.n_nodes, m.tiles);
+        if (a.vec_mode)
+            hipLaunchKernelGGL((k_fwd_csr<L, CPL, true>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
+                               a.senders, a.out);
+        else
+            hipLaunchKernelGGL((k_fwd_csr<L, CPL, false>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
+                               a.senders, a.out);
+    } else {
+        const long n = (long)a.n_nodes * Spec<L, L, L>::D3 * a.C;
+        hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, st, a.out, n);
+        if (a.n_edges > 0) {
+            dim3 grid(a.n_edges, m.tiles);
+            if (a.vec_mode)
+                hipLaunchKernelGGL((k_fwd_atomic<L, CPL, true>), grid, block, 0, st, a.n_nodes, a.C, a.x, a.y,
+                                   a.w, a.row_ptr, a.senders, a.out);
+            else
+                hipLaunchKernelGGL((k_fwd_atomic<L, CPL, false>), grid, block, 0, st, a.n_nodes, a.C, a.x, a.y,
+                                   a.w, a.row_ptr, a.senders, a.out);
+        }
+    }
+    return hipGetLastError();
+}
+
+template <int L, int CPL>
+hipError_t bwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
+    dim3 grid(a.n_nodes), block(64 * m.waves);
+    if (a.vec_mode)
+        hipLaunchKernelGGL((k_bwd_sender<L, CPL, true>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+                           a.send_ptr, a.send_perm, a.send_recv, a.dx, a.dw, a.dy);
+    else
+        hipLaunchKernelGGL((k_bwd_sender<L, CPL, false>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+                           a.send_ptr, a.send_perm, a.send_recv, a.dx, a.dw, a.dy);
+    return hipGetLastError();
+}
+
+template <int L>
+hipError_t fwd_L(const LaunchArgs& a, hipStream_t st) {
+    const ChanMap m = chan_map(a.C, kMaxThreads / 64);
+    return m.cpl == 2 ? fwd_dispatch<L, 2>(a, m, st) : fwd_dispatch<L, 1>(a, m, st);
+}
+
+template <int L>
+hipError_t bwd_L(const LaunchArgs& a, hipStream_t st) {
+    const ChanMap m = chan_map(a.C, kMaxThreads / 64);
+    return m.cpl == 2 ? bwd_dispatch<L, 2>(a, m, st) : bwd_dispatch<L, 1>(a, m, st);
+}
+
+}  // namespace
+
+bool bwd_supports_channels(int C) {
+    // the backward keeps all channels of a sender in one workgroup (deterministic dY)
+    const ChanMap m = chan_map(C, 1 << 20);
+    return m.waves <= kMaxThreads / 64;
+}
+
+hipError_t launch_fwd(const LaunchArgs& a, hipStream_t st) {
+    if (a.n_nodes == 0) return hipSuccess;
+    switch (a.L) {
+        case 0: return fwd_L<0>(a, st);
+        case 1: return fwd_L<1>(a, st);
+        case 2: return fwd_L<2>(a, st);
+        case 3: return fwd_L<3>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st) {
+    if (a.n_nodes == 0) return hipSuccess;
+    switch (a.L) {
+        case 0: return bwd_L<0>(a, st);
+        case 1: return bwd_L<1>(a, st);
+        case 2: return bwd_L<2>(a, st);
+        case 3: return bwd_L<3>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_sh(int L, long n_edges, const float* vec, float* Y, hipStream_t st) {
+    if (n_edges == 0) return hipSuccess;
+    const long D = (long)(L + 1) * (L + 1);
+    const long n = n_edges * D;
+    const dim3 block(256), grid((unsigned)((n + 255) / 256));
+    switch (L) {
+        case 0: hipLaunchKernelGGL(k_sh<0>, grid, block, 0, st, n_edges, vec, Y); break;
+        case 1: hipLaunchKernelGGL(k_sh<1>, grid, block, 0, st, n_edges, vec, Y); break;
+        case 2: hipLaunchKernelGGL(k_sh<2>, grid, block, 0, st, n_edges, vec, Y); break;
+        case 3: hipLaunchKernelGGL(k_sh<3>, grid, block, 0, st, n_edges, vec, Y); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sh_bwd(int L, long n_edges, const float* vec, const float* dY, float* dvec, hipStream_t st) {
+    if (n_edges == 0) return hipSuccess;
+    const dim3 block(256), grid((unsigned)((n_edges + 255) / 256));
+    switch (L) {
+        case 0: hipLaunchKernelGGL(k_sh_bwd<0>, grid, block, 0, st, n_edges, vec, dY, dvec); break;
+        case 1: hipLaunchKernelGGL(k_sh_bwd<1>, grid, block, 0, st, n_edges, vec, dY, dvec); break;
+        case 2: hipLaunchKernelGGL(k_sh_bwd<2>, grid, block, 0, st, n_edges, vec, dY, dvec); break;
+        case 3: hipLaunchKernelGGL(k_sh_bwd<3>, grid, block, 0, st, n_edges, vec, dY, dvec); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ctp

@@ -1,0 +1,239 @@
+// Device helpers shared by the conv tensor-product kernels: compile-time loops,
+// wavefront reductions, the per-edge coupling-slot tables and the real
+// spherical harmonics of an edge direction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <utility>
+
+#include "tables.hpp"
+
+namespace ctp {
+
+// ------------------------------------------------------------ compile-time loops
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ------------------------------------------------------------ per-slot flags
+
+// True if slot t is the first slot of its path that touches m3 (resp. m1):
+// the first product initialises a partial sum instead of accumulating.
+template <class S>
+constexpr bool first_m3(int t) {
+    for (int u = S::slot_begin[S::slots[t].p]; u < t; ++u)
+        if (S::slots[u].m3 == S::slots[t].m3) return false;
+    return true;
+}
+template <class S>
+constexpr bool first_m1(int t) {
+    for (int u = S::slot_begin[S::slots[t].p]; u < t; ++u)
+        if (S::slots[u].m1 == S::slots[t].m1) return false;
+    return true;
+}
+
+// First coupling non-zero of each path (and NNZ at the end).
+template <class S>
+constexpr int nz_begin(int p) {
+    for (int n = 0; n < S::NNZ; ++n)
+        if (S::nz[n].p >= p) return n;
+    return S::NNZ;
+}
+template <class S>
+constexpr bool nz_first_m2(int n) {
+    for (int u = nz_begin<S>(S::nz[n].p); u < n; ++u)
+        if (S::nz[u].m2 == S::nz[n].m2) return false;
+    return true;
+}
+
+// ------------------------------------------------------------ slot tables in device memory
+
+// Lane-parallel build of T_p[m1][m3] = c1 * Y[y1] + c2 * Y[y2]; y1 | (y2 << 8).
+struct SlotDev {
+    int32_t yy;
+    float c1, c2;
+};
+
+template <int L>
+struct SlotTab {
+    SlotDev s[Spec<L, L, L>::NT];
+};
+
+template <int L>
+constexpr SlotTab<L> make_slot_tab() {
+    using S = Spec<L, L, L>;
+    SlotTab<L> r{};
+    for (int t = 0; t < S::NT; ++t)
+        r.s[t] = SlotDev{S::slots[t].y1 | (S::slots[t].y2 << 8), S::slots[t].c1, S::slots[t].c2};
+    return r;
+}
+
+template <int L>
+__device__ __forceinline__ const SlotDev* slot_tab();
+
+// ------------------------------------------------------------ real spherical harmonics
+
+// Component k = l*l + l + m of the real harmonics (orthonormal, no
+// Condon-Shortley phase) of a unit vector (x, y, z):
+//   Y_k = A_m(x, y) * Q_k(z),  A_m = Re (x+iy)^m (m>0), 1 (m=0), Im (x+iy)^|m| (m<0),
+//   Q_k = N_lm * d^|m|/dz^|m| P_l(z), N_lm = sqrt((2l+1)/(4pi) (l-|m|)!/(l+|m|)!) (* sqrt2 if m != 0).
+// Legendre polynomials come from Bonnet's recurrence; Q_k is stored as
+// ascending power coefficients (degree <= 3) together with its derivative.
+struct ShCoef {
+    int32_t a;       // |m|
+    int32_t sine;    // 1 if m < 0
+    float q[4];      // Q_k(z) coefficients
+    float dq[4];     // Q_k'(z) coefficients
+};
+
+struct ShTab {
+    ShCoef k[16];
+};
+
+constexpr ShTab make_sh_tab() {
+    // Legendre P_l in the power basis, l <= 3
+    double Pl[4][4] = {};
+    Pl[0][0] = 1.0;
+    Pl[1][1] = 1.0;
+    for (int n = 1; n < 3; ++n)
+        for (int d = 0; d < 4; ++d) {
+            double v = -n * Pl[n - 1][d];
+            if (d > 0) v += (2 * n + 1) * Pl[n][d - 1];
+            Pl[n + 1][d] = v / (n + 1);
+        }
+    ShTab t{};
+    const double pi = 3.14159265358979323846;
+    for (int l = 0; l <= 3; ++l)
+        for (int m = -l; m <= l; ++m) {
+            int a = m < 0 ? -m : m;
+            double poly[4] = {Pl[l][0], Pl[l][1], Pl[l][2], Pl[l][3]};
+            for (int r = 0; r < a; ++r)           // differentiate a times
+                for (int d = 0; d < 4; ++d) poly[d] = (d + 1 < 4) ? (d + 1) * poly[d + 1] : 0.0;
+            double N = csqrt((2 * l + 1) / (4 * pi) * cfact(l - a) / cfact(l + a));
+            if (m != 0) N *= csqrt(2.0);
+            ShCoef& c = t.k[l * l + l + m];
+            c.a = a;
+            c.sine = m < 0 ? 1 : 0;
+            for (int d = 0; d < 4; ++d) c.q[d] = static_cast<float>(N * poly[d]);
+            for (int d = 0; d < 4; ++d) c.dq[d] = static_cast<float>((d + 1 < 4) ? (d + 1) * N * poly[d + 1] : 0.0);
+        }
+    return t;
+}
+
+__device__ __forceinline__ const ShTab& sh_tab();
+
+// Powers w^a = (x + iy)^a for a = 0..3 as (cos-part, sin-part).
+struct XyPow {
+    float c[4], s[4];
+};
+__device__ __forceinline__ XyPow xy_powers(float x, float y) {
+    XyPow p;
+    p.c[0] = 1.0f; p.s[0] = 0.0f;
+    p.c[1] = x;    p.s[1] = y;
+    p.c[2] = x * x - y * y;          p.s[2] = 2.0f * x * y;
+    p.c[3] = p.c[2] * x - p.s[2] * y; p.s[3] = p.c[2] * y + p.s[2] * x;
+    return p;
+}
+
+__device__ __forceinline__ float pick4(const float* v, int a) {
+    float r = v[0];
+    r = (a == 1) ? v[1] : r;
+    r = (a == 2) ? v[2] : r;
+    r = (a == 3) ? v[3] : r;
+    return r;
+}
+
+__device__ __forceinline__ float horner4(const float* q, float z) {
+    return ((q[3] * z + q[2]) * z + q[1]) * z + q[0];
+}
+
+// Y_k of the direction of v; |v| = 0 gives Y_0 = 1/sqrt(4pi) and 0 otherwise.
+__device__ __forceinline__ float sh_component(int k, float vx, float vy, float vz) {
+    const float n2 = vx * vx + vy * vy + vz * vz;
+    if (n2 == 0.0f) return k == 0 ? 0.28209479177387814f : 0.0f;
+    const float inv = 1.0f / sqrtf(n2);
+    const float x = vx * inv, y = vy * inv, z = vz * inv;
+    const ShCoef& c = sh_tab().k[k];
+    const XyPow p = xy_powers(x, y);
+    const float A = c.sine ? pick4(p.s, c.a) : pick4(p.c, c.a);
+    return A * horner4(c.q, z);
+}
+
+// dY_k / dr (gradient of the polynomial form at the unit vector r).
+__device__ __forceinline__ void sh_component_grad(int k, float x, float y, float z, float g[3]) {
+    const ShCoef& c = sh_tab().k[k];
+    const XyPow p = xy_powers(x, y);
+    const float Q = horner4(c.q, z), dQ = horner4(c.dq, z);
+    const int a = c.a;
+    const float fa = static_cast<float>(a);
+    const int am1 = a > 0 ? a - 1 : 0;
+    const float cm = pick4(p.c, am1), sm = pick4(p.s, am1);
+    float A, dAx, dAy;
+    if (c.sine) {
+        A = pick4(p.s, a);
+        dAx = fa * sm;
+        dAy = fa * cm;
+    } else {
+        A = pick4(p.c, a);
+        dAx = fa * cm;
+        dAy = -fa * sm;
+    }
+    g[0] = dAx * Q;
+    g[1] = dAy * Q;
+    g[2] = A * dQ;
+}
+
+// ------------------------------------------------------------ wavefront reductions (wave64, DPP)
+
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ float dpp_t(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, RowMask, 0xf, false));
+}
+
+// Sum over the 64 lanes, in a fixed order; the total is valid in lane 63.
+__device__ __forceinline__ float wave_sum_to_last(float v) {
+    v += dpp_t<0xB1>(v);          // quad_perm [1,0,3,2]
+    v += dpp_t<0x4E>(v);          // quad_perm [2,3,0,1]
+    v += dpp_t<0x124>(v);         // row_ror:4
+    v += dpp_t<0x128>(v);         // row_ror:8  -> every lane holds its row sum
+    v += dpp_t<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v += dpp_t<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ------------------------------------------------------------ vector loads
+
+template <int CPL>
+__device__ __forceinline__ void load_ch(const float* __restrict__ p, float (&v)[CPL]) {
+    if constexpr (CPL == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(p);
+        v[0] = t.x;
+        v[1] = t.y;
+    } else {
+        v[0] = p[0];
+    }
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_ch(float* __restrict__ p, const float (&v)[CPL]) {
+    if constexpr (CPL == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+        p[0] = v[0];
+    }
+}
+
+}  // namespace ctp

@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI front and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ctp {
+
+struct LaunchArgs {
+    int L;                 // l_in = l_sh = l_out
+    int n_nodes, n_edges, C;
+    int algo;              // 0: CSR deterministic, 1: edge-parallel atomic (forward only)
+    int vec_mode;          // 0: Y[E][D] given, 1: vec[E][3] given
+    const float* x;        // [N][D][C]
+    const float* y;        // Y[E][D] or vec[E][3]
+    const float* w;        // [E][P][C]
+    const float* grad;     // [N][D][C] (backward)
+    const int32_t* row_ptr;
+    const int32_t* senders;
+    const int32_t* send_ptr;
+    const int32_t* send_perm;
+    const int32_t* send_recv;
+    float* out;            // forward output
+    float* dx;             // [N][D][C]
+    float* dw;             // [E][P][C]
+    float* dy;             // dY[E][D] or dvec[E][3]
+};
+
+hipError_t launch_fwd(const LaunchArgs& a, hipStream_t st);
+hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st);
+bool bwd_supports_channels(int C);
+hipError_t launch_sh(int L, long n_edges, const float* vec, float* Y, hipStream_t st);
+hipError_t launch_sh_bwd(int L, long n_edges, const float* vec, const float* dY, float* dvec, hipStream_t st);
+
+hipError_t launch_transpose(int n_nodes, int n_edges, const int32_t* row_ptr, const int32_t* senders,
+                            int32_t* send_ptr, int32_t* send_perm, int32_t* send_recv, hipStream_t st);
+hipError_t launch_check_graph(int n_nodes, int n_edges, const int32_t* row_ptr, const int32_t* senders,
+                              unsigned long long* d_bad, hipStream_t st);
+
+}  // namespace ctp

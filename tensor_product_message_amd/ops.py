@@ -1,0 +1,213 @@
+"""Torch-facing binding of libconvtp.so: argument marshalling only.
+
+Every computation runs in the library's HIP kernels; this module checks
+tensor metadata, passes raw device pointers and the current HIP stream, and
+turns a non-zero status into `ConvTPError`.  PyTorch provides device memory
+and streams, nothing else.
+
+Shapes (channel index fastest, D_l = (l+1)^2, P = num_paths(l)):
+    x, out, grad_out, dx : [N, D, C] float32
+    w, dw                : [E, P, C] float32
+    Y, dY                : [E, D]    float32  (y_mode 0)
+    vec, dvec            : [E, 3]    float32  (y_mode 1)
+    row_ptr [N+1], senders [E], send_ptr [N+1], send_perm [E], send_recv [E]: int32
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _capi
+from ._capi import ConvTPError, Problem, check, lib  # noqa: F401
+
+Y_GIVEN, VEC_GIVEN = 0, 1
+ALGO_CSR, ALGO_ATOMIC = 0, 1
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _want(t, name, shape, dtype=torch.float32, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def dim(l: int) -> int:
+    return (l + 1) ** 2
+
+
+def num_paths(l_in: int, l_sh: int = None, l_out: int = None) -> int:
+    l_sh = l_in if l_sh is None else l_sh
+    l_out = l_in if l_out is None else l_out
+    n = lib().conv_tp_num_paths(l_in, l_sh, l_out)
+    if n < 0:
+        raise ConvTPError(_capi.CTP_EUNSUPPORTED, lib().conv_tp_last_error().decode())
+    return n
+
+
+def paths(l_in: int, l_sh: int = None, l_out: int = None):
+    l_sh = l_in if l_sh is None else l_sh
+    l_out = l_in if l_out is None else l_out
+    n = num_paths(l_in, l_sh, l_out)
+    buf = np.zeros((n, 3), dtype=np.int32)
+    check(lib().conv_tp_paths(l_in, l_sh, l_out, buf.ctypes.data_as(ctypes.c_void_p)))
+    return [tuple(int(v) for v in r) for r in buf]
+
+
+def coupling(l1: int, l2: int, l3: int) -> np.ndarray:
+    out = np.zeros((2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1), dtype=np.float64)
+    check(lib().conv_tp_coupling(l1, l2, l3, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+class Graph:
+    """A static CSR-by-receiver graph on a device, with its sender transpose.
+
+    The transpose (send_ptr, send_perm, send_recv) is built once by
+    conv_tp_build_transpose and reused by every backward pass.
+    """
+
+    def __init__(self, n_nodes: int, row_ptr: torch.Tensor, senders: torch.Tensor):
+        self.n_nodes = int(n_nodes)
+        self.n_edges = int(senders.numel())
+        _want(row_ptr, "row_ptr", (self.n_nodes + 1,), torch.int32)
+        _want(senders, "senders", (self.n_edges,), torch.int32, row_ptr.device)
+        self.row_ptr, self.senders = row_ptr, senders
+        self.device = row_ptr.device
+        self._t = None
+
+    @property
+    def transpose(self):
+        if self._t is None:
+            self._t = build_transpose(self.n_nodes, self.row_ptr, self.senders)
+        return self._t
+
+    def check(self) -> int:
+        return check_graph(self.n_nodes, self.row_ptr, self.senders)
+
+
+def build_transpose(n_nodes: int, row_ptr: torch.Tensor, senders: torch.Tensor):
+    n_edges = senders.numel()
+    _want(row_ptr, "row_ptr", (n_nodes + 1,), torch.int32)
+    _want(senders, "senders", (n_edges,), torch.int32, row_ptr.device)
+    dev = row_ptr.device
+    send_ptr = torch.empty(n_nodes + 1, dtype=torch.int32, device=dev)
+    send_perm = torch.empty(n_edges, dtype=torch.int32, device=dev)
+    send_recv = torch.empty(n_edges, dtype=torch.int32, device=dev)
+    check(lib().conv_tp_build_transpose(n_nodes, n_edges, _p(row_ptr), _p(senders), _p(send_ptr),
+                                        _p(send_perm), _p(send_recv), _stream(row_ptr)))
+    return send_ptr, send_perm, send_recv
+
+
+def check_graph(n_nodes: int, row_ptr: torch.Tensor, senders: torch.Tensor) -> int:
+    n_edges = senders.numel()
+    _want(row_ptr, "row_ptr", (n_nodes + 1,), torch.int32)
+    _want(senders, "senders", (n_edges,), torch.int32, row_ptr.device)
+    bad = ctypes.c_int64(0)
+    check(lib().conv_tp_check_graph(n_nodes, n_edges, _p(row_ptr), _p(senders), ctypes.byref(bad),
+                                    _stream(row_ptr)))
+    return int(bad.value)
+
+
+def _problem(n_nodes, n_edges, channels, lmax, y_mode, algo) -> Problem:
+    return Problem(n_nodes, n_edges, channels, lmax, lmax, lmax, y_mode, algo)
+
+
+def _shapes(x, y_or_vec, w, graph, lmax, y_mode):
+    n, e = graph.n_nodes, graph.n_edges
+    if x.dim() != 3:
+        raise ValueError("x must be [N, D, C]")
+    c = x.shape[2]
+    _want(x, "x", (n, dim(lmax), c), device=graph.device)
+    _want(y_or_vec, "y_or_vec", (e, dim(lmax) if y_mode == Y_GIVEN else 3), device=graph.device)
+    _want(w, "w", (e, num_paths(lmax), c), device=graph.device)
+    return n, e, c
+
+
+def conv_tp_fwd(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN, algo: int = ALGO_CSR,
+                out=None):
+    """out[N, D, C] = conv(x, Y or vec, w) on `graph` (see include/convtp.h)."""
+    n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode)
+    if out is None:
+        out = torch.empty((n, dim(lmax), c), dtype=torch.float32, device=x.device)
+    _want(out, "out", (n, dim(lmax), c), device=x.device)
+    prob = _problem(n, e, c, lmax, y_mode, algo)
+    check(lib().conv_tp_fwd(ctypes.byref(prob), _p(x), _p(y_or_vec), _p(w), _p(graph.row_ptr),
+                            _p(graph.senders), _p(out), _stream(x)))
+    return out
+
+
+def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN,
+                dx=None, dw=None, dy=None):
+    """(dx, dw, dY or dvec) for upstream gradient grad_out (see include/convtp.h)."""
+    n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode)
+    _want(grad_out, "grad_out", (n, dim(lmax), c), device=x.device)
+    send_ptr, send_perm, send_recv = graph.transpose
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w) if dw is None else dw
+    dy = torch.empty_like(y_or_vec) if dy is None else dy
+    _want(dx, "dx", x.shape, device=x.device)
+    _want(dw, "dw", w.shape, device=x.device)
+    _want(dy, "dy", y_or_vec.shape, device=x.device)
+    prob = _problem(n, e, c, lmax, y_mode, ALGO_CSR)
+    check(lib().conv_tp_bwd(ctypes.byref(prob), _p(grad_out), _p(x), _p(y_or_vec), _p(w),
+                            _p(graph.row_ptr), _p(graph.senders), _p(send_ptr), _p(send_perm),
+                            _p(send_recv), _p(dx), _p(dw), _p(dy), _stream(x)))
+    return dx, dw, dy
+
+
+def spherical_harmonics(vec, lmax: int, out=None):
+    e = vec.shape[0]
+    _want(vec, "vec", (e, 3))
+    out = torch.empty((e, dim(lmax)), dtype=torch.float32, device=vec.device) if out is None else out
+    _want(out, "Y", (e, dim(lmax)), device=vec.device)
+    check(lib().conv_tp_sh(e, lmax, _p(vec), _p(out), _stream(vec)))
+    return out
+
+
+def spherical_harmonics_backward(vec, dY, lmax: int, out=None):
+    e = vec.shape[0]
+    _want(vec, "vec", (e, 3))
+    _want(dY, "dY", (e, dim(lmax)), device=vec.device)
+    out = torch.empty_like(vec) if out is None else out
+    _want(out, "dvec", (e, 3), device=vec.device)
+    check(lib().conv_tp_sh_bwd(e, lmax, _p(vec), _p(dY), _p(out), _stream(vec)))
+    return out
+
+
+class ConvTPFunction(torch.autograd.Function):
+    """Autograd wrapper: forward = conv_tp_fwd (algo 0), backward = conv_tp_bwd."""
+
+    @staticmethod
+    def forward(ctx, x, y_or_vec, w, graph, lmax, y_mode):
+        ctx.save_for_backward(x, y_or_vec, w)
+        ctx.graph, ctx.lmax, ctx.y_mode = graph, lmax, y_mode
+        return conv_tp_fwd(x, y_or_vec, w, graph, lmax, y_mode)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        x, y_or_vec, w = ctx.saved_tensors
+        dx, dw, dy = conv_tp_bwd(grad_out.contiguous(), x, y_or_vec, w, ctx.graph, ctx.lmax, ctx.y_mode)
+        return dx, dy, dw, None, None, None
+
+
+def conv_tp(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN):
+    """Differentiable fused convolution tensor product."""
+    return ConvTPFunction.apply(x, y_or_vec, w, graph, lmax, y_mode)

@@ -1,0 +1,148 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, answers path/coupling queries like the oracle, and rejects
+every invalid argument on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import cg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def capi():
+    from tensor_product_message_amd import _capi
+    if not os.path.exists(_capi.LIB_PATH):
+        from tensor_product_message_amd.build import build
+        build(verbose=False)
+    return _capi
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "convtp.h")).read()
+    return sorted(set(re.findall(r"\b(conv_tp_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(capi):
+    L = capi.lib()
+    declared = _header_functions()
+    assert set(declared) == set(capi.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.conv_tp_version() == 100
+
+
+def test_paths_match_oracle(capi):
+    import tensor_product_message_amd as t
+    for L in range(4):
+        assert t.num_paths(L) == len(cg.paths(L, L, L))
+        assert t.paths(L) == cg.paths(L, L, L)
+    assert t.paths(0, 3, 3) == cg.paths(0, 3, 3)
+
+
+def test_coupling_tables_match_oracle(capi):
+    import tensor_product_message_amd as t
+    for p in cg.paths(3, 3, 3):
+        np.testing.assert_allclose(t.coupling(*p), cg.real_cg(*p), atol=1e-14, rtol=0)
+        # identical structural zeros
+        assert np.array_equal(t.coupling(*p) != 0, cg.real_cg(*p) != 0)
+
+
+def _prob(capi, **kw):
+    d = dict(n_nodes=4, n_edges=8, channels=16, l_in=1, l_sh=1, l_out=1, y_mode=0, algo=0)
+    d.update(kw)
+    return capi.Problem(**d)
+
+
+A = ctypes.c_void_p(0x10000)          # aligned fake addresses: validation must fail first
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)        # 4-byte aligned only
+NUL = ctypes.c_void_p(0)
+
+
+def _fwd(capi, prob, x=A, y=A, w=A, rp=A, s=A, out=A2):
+    return capi.lib().conv_tp_fwd(ctypes.byref(prob) if prob is not None else None, x, y, w, rp, s, out, NUL)
+
+
+def _bwd(capi, prob, g=A, x=A, y=A, w=A, rp=A, s=A, sp=A, pe=A, sr=A, dx=A2, dw=A2, dy=A2):
+    return capi.lib().conv_tp_bwd(ctypes.byref(prob), g, x, y, w, rp, s, sp, pe, sr, dx, dw, dy, NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_nodes=-1), 1), (dict(n_edges=-3), 1), (dict(channels=0), 1),
+    (dict(channels=1025), 2), (dict(l_in=4, l_sh=4, l_out=4), 2), (dict(l_in=-1), 2),
+    (dict(l_in=1, l_sh=2, l_out=2), 2), (dict(y_mode=2), 1), (dict(algo=7), 1),
+    (dict(n_nodes=0, n_edges=5), 5),
+])
+def test_fwd_rejects_bad_problem(capi, kw, code):
+    assert _fwd(capi, _prob(capi, **kw)) == code
+    assert capi.lib().conv_tp_last_error().decode()
+
+
+def test_fwd_rejects_bad_pointers(capi):
+    p = _prob(capi)
+    assert _fwd(capi, None) == capi.CTP_EINVAL
+    assert _fwd(capi, p, x=NUL) == capi.CTP_EINVAL
+    assert _fwd(capi, p, y=NUL) == capi.CTP_EINVAL
+    assert _fwd(capi, p, w=NUL) == capi.CTP_EINVAL
+    assert _fwd(capi, p, rp=NUL) == capi.CTP_EINVAL
+    assert _fwd(capi, p, s=NUL) == capi.CTP_EINVAL
+    assert _fwd(capi, p, out=NUL) == capi.CTP_EINVAL
+    assert _fwd(capi, p, x=MIS) == capi.CTP_EALIGN
+    assert _fwd(capi, p, w=MIS) == capi.CTP_EALIGN
+    assert _fwd(capi, p, out=MIS) == capi.CTP_EALIGN
+    assert _fwd(capi, p, rp=ctypes.c_void_p(0x10002)) == capi.CTP_EALIGN
+    assert "aligned" in capi.lib().conv_tp_last_error().decode()
+
+
+def test_bwd_rejections(capi):
+    assert _bwd(capi, _prob(capi, algo=1)) == capi.CTP_EUNSUPPORTED
+    assert _bwd(capi, _prob(capi, channels=1024)) == capi.CTP_EUNSUPPORTED
+    assert _bwd(capi, _prob(capi, channels=320)) == capi.CTP_EUNSUPPORTED
+    p = _prob(capi)
+    for k in ("g", "x", "y", "w", "rp", "s", "sp", "pe", "sr", "dx", "dw", "dy"):
+        assert _bwd(capi, p, **{k: NUL}) == capi.CTP_EINVAL, k
+    assert _bwd(capi, p, dw=MIS) == capi.CTP_EALIGN
+    assert _bwd(capi, p, g=MIS) == capi.CTP_EALIGN
+
+
+def test_empty_arrays_may_be_null(capi):
+    # N = 0, E = 0: only row_ptr (one element) is required; the call then
+    # succeeds without any kernel, so it is safe without a GPU only if it
+    # returns before touching the device -- it does: nothing to launch.
+    L = capi.lib()
+    p = _prob(capi, n_nodes=0, n_edges=0)
+    assert _fwd(capi, p, x=NUL, y=NUL, w=NUL, s=NUL, out=NUL) == capi.CTP_OK
+    assert _fwd(capi, p, rp=NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_sh(0, 2, NUL, NUL, NUL) == capi.CTP_OK
+
+
+def test_other_entry_points_validate(capi):
+    L = capi.lib()
+    assert L.conv_tp_num_paths(4, 1, 1) == -1
+    assert L.conv_tp_num_paths(2, 2, 2) == 15 and L.conv_tp_last_error().decode() == ""
+    assert L.conv_tp_paths(1, 1, 1, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_coupling(0, 1, 2, A) == capi.CTP_EINVAL
+    assert L.conv_tp_coupling(4, 1, 3, A) == capi.CTP_EUNSUPPORTED
+    assert L.conv_tp_sh(-1, 2, A, A, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_sh(5, 4, A, A, NUL) == capi.CTP_EUNSUPPORTED
+    assert L.conv_tp_sh(5, 2, NUL, A, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_sh_bwd(5, 2, A, A, NUL, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_build_transpose(-1, 0, A, A, A, A, A, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_build_transpose(0, 3, A, A, A, A, A, NUL) == capi.CTP_EGRAPH
+    assert L.conv_tp_build_transpose(4, 3, A, A, NUL, A, A, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_build_transpose(4, 3, A, MIS, A, A, ctypes.c_void_p(0x10001), NUL) == capi.CTP_EALIGN
+    assert L.conv_tp_check_graph(4, 3, A, A, None, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_check_graph(4, -3, A, A, None, NUL) == capi.CTP_EINVAL
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from tensor_product_message_amd import _capi
+    monkeypatch.setattr(_capi, "_lib", None)
+    monkeypatch.setattr(_capi, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _capi.lib()

@@ -1,0 +1,348 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bar: for every output tensor, max |gpu - oracle| <= 1e-4 * max |oracle|
+(fp32 kernels vs fp64 oracle); index arrays bit-exact; the deterministic
+kernels bitwise reproducible run to run.  Small workloads are compared
+element by element; full-size workloads on seeded samples of receivers,
+senders and edges that the oracle evaluates one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import convtp as oc
+from oracle import graph as og
+from oracle import sh as osh
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+RTOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_product_message_amd  # noqa: F401  (fails loudly if the library is missing)
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ctp(dev):
+    import tensor_product_message_amd as t
+    return t
+
+
+def close(name, got, ref, nonzero=True):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    if nonzero:
+        assert scale > 0.0, f"{name}: reference is identically zero"
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    assert np.isfinite(got).all(), name
+    assert err <= RTOL * scale or err == 0.0, f"{name}: max err {err:.3e} vs scale {scale:.3e}"
+
+
+def T(a, dev, dtype=None):
+    t = torch.as_tensor(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def sh32(L, vec):
+    return osh.real_sh(L, np.asarray(vec, dtype=np.float64)).astype(np.float32)
+
+
+# ------------------------------------------------------------ small workloads, full comparison
+
+
+def run_small(ctp, dev, d, L, y_mode, algo=0, bwd=True):
+    n, e = d["n_nodes"], d["n_edges"]
+    prob = oc.Problem(L, L, L)
+    vec = d["vec"]
+    Y = sh32(L, vec)
+    yin = Y if y_mode == 0 else vec
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w = T(d["x"], dev), T(d["w"], dev)
+    yv = T(yin, dev)
+    out = ctp.conv_tp_fwd(x, yv, w, g, L, y_mode, algo)
+    # oracle: Y mode sees the same fp32 Y; vec mode sees fp64 harmonics of the same vec
+    Yref = Y.astype(np.float64) if y_mode == 0 else osh.real_sh(L, vec.astype(np.float64))
+    ref = oc.fwd(prob, d["x"], Yref, d["w"], d["row_ptr"], d["senders"])
+    close("out", host(out), ref)
+    if not bwd:
+        return
+    G = T(d["grad_out"], dev)
+    dx, dw, dy = ctp.conv_tp_bwd(G, x, yv, w, g, L, y_mode)
+    sp, pe, sr = og.transpose(n, d["row_ptr"], d["senders"])
+    close("dx", host(dx), oc.bwd_dx(prob, Yref, d["w"], d["grad_out"], sp, pe, sr))
+    dw_ref, dY_ref = oc.bwd_edges(prob, d["x"], Yref, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+    close("dw", host(dw), dw_ref)
+    if y_mode == 0:
+        close("dY", host(dy), dY_ref)
+    else:
+        close("dvec", host(dy), osh.vec_grad_from_sh_grad(L, vec.astype(np.float64), dY_ref))
+
+
+@pytest.mark.parametrize("y_mode", [0, 1])
+@pytest.mark.parametrize("algo", [0, 1])
+def test_tiny(ctp, dev, y_mode, algo):
+    run_small(ctp, dev, gen.tiny(), 1, y_mode, algo, bwd=(algo == 0))
+
+
+SMALL = [  # (N, C, L): several channel tiles, ragged lane tails, every degree
+    (90, 16, 1), (150, 48, 2), (120, 128, 2), (100, 128, 3), (70, 64, 3),
+    (60, 192, 3), (50, 256, 2), (40, 512, 2), (30, 1024, 2), (40, 96, 0), (60, 128, 0),
+]
+
+
+@pytest.mark.parametrize("n,c,L", SMALL)
+@pytest.mark.parametrize("y_mode", [0, 1])
+def test_small_poisson(ctp, dev, n, c, L, y_mode):
+    d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=n + c + L)
+    bwd_ok = (c % 128 == 0 and c <= 512) or c <= 256
+    run_small(ctp, dev, d, L, y_mode, 0, bwd=bwd_ok)
+    run_small(ctp, dev, d, L, y_mode, 1, bwd=False)
+
+
+def test_deterministic_reruns(ctp, dev):
+    d = gen.poisson_small(300, 128, 3, mean_deg=45.0, seed=5)
+    g = ctp.Graph(300, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w, G = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev)
+    for y_mode, y in ((0, T(sh32(3, d["vec"]), dev)), (1, T(d["vec"], dev))):
+        a = ctp.conv_tp_fwd(x, y, w, g, 3, y_mode)
+        b = ctp.conv_tp_fwd(x, y, w, g, 3, y_mode)
+        assert torch.equal(a, b)
+        r1 = ctp.conv_tp_bwd(G, x, y, w, g, 3, y_mode)
+        r2 = ctp.conv_tp_bwd(G, x, y, w, g, 3, y_mode)
+        for u, v in zip(r1, r2):
+            assert torch.equal(u, v)
+
+
+# ------------------------------------------------------------ bookkeeping and harmonics
+
+
+@pytest.mark.parametrize("which", ["tiny", "poisson", "water", "skewed"])
+def test_transpose_bit_exact(ctp, dev, which):
+    if which == "tiny":
+        d = gen.tiny()
+        n, rp, s = d["n_nodes"], d["row_ptr"], d["senders"]
+    elif which == "poisson":
+        n = 20000
+        rp, s = gen.poisson_graph(n, 45.0, np.random.default_rng(3))
+    elif which == "water":
+        d = gen.water_box_graph()
+        n, rp, s = d["n_nodes"], d["row_ptr"], d["senders"]
+    else:   # one sender with 3000 out-edges, many isolated nodes
+        n = 500
+        rng = np.random.default_rng(4)
+        recv = np.sort(rng.integers(0, n, size=4000))
+        s = rng.integers(0, n, size=4000).astype(np.int32)
+        s[rng.choice(4000, 3000, replace=False)] = 7
+        rp = og.row_ptr_from_receivers(recv, n)
+    ref = og.transpose(n, rp, s)
+    got = ctp.build_transpose(n, T(rp, dev), T(s, dev))
+    for a, b in zip(got, ref):
+        assert np.array_equal(host(a), b)
+    assert ctp.check_graph(n, T(rp, dev), T(s, dev)) == 0
+
+
+def test_check_graph_counts_defects(ctp, dev):
+    n = 50
+    rp, s = gen.poisson_graph(n, 6.0, np.random.default_rng(8))
+    bad_s = s.copy()
+    bad_s[[1, 5, 9]] = [n, -2, n + 100]
+    bad_rp = rp.copy()
+    bad_rp[10] = bad_rp[11] + 3
+    for r, q in ((rp, bad_s), (bad_rp, s), (bad_rp, bad_s)):
+        assert ctp.check_graph(n, T(r, dev), T(q, dev)) == og.check_graph(n, r, q)
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3])
+def test_spherical_harmonics(ctp, dev, L):
+    rng = np.random.default_rng(L)
+    vec = (rng.standard_normal((5000, 3)) * rng.uniform(0.1, 10, size=(5000, 1))).astype(np.float32)
+    vec[0] = 0.0
+    vec[1] = (0.0, 0.0, 2.5)       # pole
+    vec[2] = (0.0, 0.0, -1e-3)
+    Y = ctp.spherical_harmonics(T(vec, dev), L)
+    close("Y", host(Y), osh.real_sh(L, vec.astype(np.float64)))
+    dY = rng.standard_normal((5000, (L + 1) ** 2)).astype(np.float32)
+    dv = ctp.spherical_harmonics_backward(T(vec, dev), T(dY, dev), L)
+    close("dvec", host(dv), osh.vec_grad_from_sh_grad(L, vec.astype(np.float64), dY))
+    assert not host(dv)[0].any()
+
+
+# ------------------------------------------------------------ edge cases
+
+
+def test_empty_graph_gives_zeros(ctp, dev):
+    n, c, L = 5, 128, 2
+    rp = np.zeros(n + 1, dtype=np.int32)
+    s = np.zeros(0, dtype=np.int32)
+    g = ctp.Graph(n, T(rp, dev), T(s, dev))
+    x = torch.randn(n, 9, c, device=dev)
+    w = torch.empty(0, 15, c, device=dev)
+    y = torch.empty(0, 9, device=dev)
+    for algo in (0, 1):
+        out = ctp.conv_tp_fwd(x, y, w, g, L, 0, algo)
+        assert not out.any()
+    dx, dw, dy = ctp.conv_tp_bwd(torch.randn_like(x), x, y, w, g, L, 0)
+    assert not dx.any() and dw.numel() == 0 and dy.numel() == 0
+
+
+def test_hub_self_edges_duplicates_and_zero_vectors(ctp, dev):
+    """One receiver with in-degree 1000, isolated nodes, explicit self-edges,
+    duplicate edges, zero-weight edges and zero edge vectors."""
+    rng = np.random.default_rng(12)
+    n, c, L = 40, 128, 3
+    recv = np.concatenate([np.full(1000, 3), rng.integers(0, n, size=300)])
+    recv[recv == 17] = 18                        # node 17 has no incoming edge
+    recv = np.sort(recv)
+    s = rng.integers(0, n, size=recv.size)
+    s[s == 21] = 22                              # node 21 sends nothing
+    s[:10] = recv[:10]                           # self-edges
+    s[10:20] = s[20:30]
+    rp = og.row_ptr_from_receivers(recv, n)
+    e = recv.size
+    vec = rng.standard_normal((e, 3)).astype(np.float32)
+    vec[::37] = 0.0
+    w = rng.standard_normal((e, 34, c)).astype(np.float32)
+    w[::5] = 0.0
+    d = dict(n_nodes=n, n_edges=e, row_ptr=rp, senders=s.astype(np.int32), vec=vec,
+             x=rng.standard_normal((n, 16, c)).astype(np.float32), w=w,
+             grad_out=rng.standard_normal((n, 16, c)).astype(np.float32))
+    for y_mode in (0, 1):
+        run_small(ctp, dev, d, L, y_mode, 0)
+        run_small(ctp, dev, d, L, y_mode, 1, bwd=False)
+
+
+# ------------------------------------------------------------ full-size workloads, sampled
+
+
+def _sub_fwd(prob, rp, s, Yref, w_dev, x_host, rows):
+    edges = np.concatenate([np.arange(rp[i], rp[i + 1]) for i in rows]).astype(np.int64)
+    rp_sub = np.zeros(len(rows) + 1, dtype=np.int32)
+    rp_sub[1:] = np.cumsum([rp[i + 1] - rp[i] for i in rows])
+    w_sub = host(w_dev[torch.as_tensor(edges, device=w_dev.device)])
+    # receivers renumbered 0..len(rows)-1; senders stay global
+    return oc.fwd(prob, x_host, Yref[edges], w_sub, rp_sub, s[edges], rows=np.arange(len(rows)))
+
+
+def _sub_dx(prob, rp, s, Yref, w_dev, G_host, senders_sel):
+    recv = og.receivers_of(rp)
+    pos = {j: k for k, j in enumerate(senders_sel)}
+    edges = np.nonzero(np.isin(s, senders_sel))[0]
+    loc = np.array([pos[j] for j in s[edges]], dtype=np.int64)
+    order = np.argsort(loc, kind="stable")
+    send_ptr = np.zeros(len(senders_sel) + 1, dtype=np.int32)
+    send_ptr[1:] = np.cumsum(np.bincount(loc, minlength=len(senders_sel)))
+    w_sub = host(w_dev[torch.as_tensor(edges, device=w_dev.device)])
+    return oc.bwd_dx(prob, Yref[edges], w_sub, G_host, send_ptr, order.astype(np.int32),
+                     recv[edges][order].astype(np.int32), rows=np.arange(len(senders_sel)))
+
+
+def _sub_edges(prob, rp, s, Yref, w_dev, x_host, G_host, edges):
+    recv = og.receivers_of(rp)[edges]
+    rp_sub = og.row_ptr_from_receivers(recv, len(rp) - 1)
+    w_sub = host(w_dev[torch.as_tensor(edges, device=w_dev.device)])
+    return oc.bwd_edges(prob, x_host, Yref[edges], w_sub, G_host, rp_sub, s[edges])
+
+
+def run_full(ctp, dev, n, c, L, y_mode, algo=0, bwd=False, seed=0, n_sample=48):
+    d = gen.poisson_full(n, c, L, dev, seed=seed, need_grad=bwd)
+    rp, s, vec = d["row_ptr"], d["senders"], d["vec"]
+    prob = oc.Problem(L, L, L)
+    Y = sh32(L, vec)
+    yin = T(Y if y_mode == 0 else vec, dev)
+    Yref = Y.astype(np.float64) if y_mode == 0 else osh.real_sh(L, vec.astype(np.float64))
+    g = ctp.Graph(n, T(rp, dev), T(s, dev))
+    out = ctp.conv_tp_fwd(d["x"], yin, d["w"], g, L, y_mode, algo)
+    rng = np.random.default_rng(seed + 99)
+    rows = np.sort(rng.choice(n, n_sample, replace=False))
+    x_host = host(d["x"])
+    close("out[sample]", host(out[torch.as_tensor(rows, device=dev)]),
+          _sub_fwd(prob, rp, s, Yref, d["w"], x_host, rows))
+    del out
+    if not bwd:
+        return
+    dx, dw, dy = ctp.conv_tp_bwd(d["grad_out"], d["x"], yin, d["w"], g, L, y_mode)
+    G_host = host(d["grad_out"])
+    close("dx[sample]", host(dx[torch.as_tensor(rows, device=dev)]),
+          _sub_dx(prob, rp, s, Yref, d["w"], G_host, rows))
+    edges = np.sort(rng.choice(len(s), 4 * n_sample, replace=False))
+    dw_ref, dY_ref = _sub_edges(prob, rp, s, Yref, d["w"], x_host, G_host, edges)
+    ei = torch.as_tensor(edges, device=dev)
+    close("dw[sample]", host(dw[ei]), dw_ref)
+    if y_mode == 0:
+        close("dY[sample]", host(dy[ei]), dY_ref)
+    else:
+        close("dvec[sample]", host(dy[ei]), osh.vec_grad_from_sh_grad(L, vec[edges].astype(np.float64), dY_ref))
+
+
+def test_full_l2_forward(ctp, dev):
+    """lmax=2, N=32768, C=128 (N*C = 2^22), Poisson(45) in-degrees."""
+    run_full(ctp, dev, 32768, 128, 2, 0)
+
+
+@pytest.mark.parametrize("y_mode", [0, 1])
+def test_full_l3_forward_backward(ctp, dev, y_mode):
+    """lmax=3, N=16384, C=128 (N*C = 2^21), forward and backward."""
+    run_full(ctp, dev, 16384, 128, 3, y_mode, bwd=True)
+
+
+@pytest.mark.parametrize("c", gen.SWEEP_CHANNELS)
+@pytest.mark.parametrize("algo", [0, 1])
+def test_full_channel_sweep(ctp, dev, c, algo):
+    """lmax=2 forward, N = 2^22 / C, both the CSR and the atomic variant."""
+    run_full(ctp, dev, (1 << 22) // c, c, 2, 0, algo=algo, n_sample=24)
+    torch.cuda.empty_cache()
+
+
+def test_water_box_two_layers(ctp, dev):
+    """1503 atoms, 83,325 padded edges, C=128, lmax=3, vec mode: two chained
+    layers forward, then backward to the edge vectors (sum of both layers)."""
+    wb = gen.water_box(seed=0, device="cpu")
+    n, L = wb["n_nodes"], 3
+    prob = oc.Problem(L, L, L)
+    vec = wb["vec"]
+    g = ctp.Graph(n, T(wb["row_ptr"], dev), T(wb["senders"], dev))
+    v = T(vec, dev)
+    w1, w2 = wb["w1"].numpy(), wb["w2"].numpy()
+    x0 = T(wb["x"], dev)
+    h1 = ctp.conv_tp_fwd(x0, v, T(w1, dev), g, L, 1)
+    h2 = ctp.conv_tp_fwd(h1, v, T(w2, dev), g, L, 1)
+    G = T(wb["grad_out"], dev)
+    dh1, dw2, dv2 = ctp.conv_tp_bwd(G, h1, v, T(w2, dev), g, L, 1)
+    dx0, dw1, dv1 = ctp.conv_tp_bwd(dh1, x0, v, T(w1, dev), g, L, 1)
+    # oracle chain from the same inputs (C edge loop, fp64 accumulation; its
+    # fp64 layer-1 results are rounded to fp32 where they feed layer 2)
+    Yref = osh.real_sh(L, vec.astype(np.float64))
+    rp, s = wb["row_ptr"], wb["senders"]
+    sp, pe, sr = og.transpose(n, rp, s)
+    r1 = oc.fwd(prob, wb["x"], Yref, w1, rp, s)
+    r2 = oc.fwd(prob, r1, Yref, w2, rp, s)
+    close("h1", host(h1), r1)
+    close("h2", host(h2), r2)
+    rdh1 = oc.bwd_dx(prob, Yref, w2, wb["grad_out"], sp, pe, sr)
+    rdw2, rdY2 = oc.bwd_edges(prob, r1, Yref, w2, wb["grad_out"], rp, s)
+    rdx0 = oc.bwd_dx(prob, Yref, w1, rdh1, sp, pe, sr)
+    rdw1, rdY1 = oc.bwd_edges(prob, wb["x"], Yref, w1, rdh1, rp, s)
+    close("dh1", host(dh1), rdh1)
+    close("dx0", host(dx0), rdx0)
+    close("dw1", host(dw1), rdw1)
+    close("dw2", host(dw2), rdw2)
+    dvec_ref = osh.vec_grad_from_sh_grad(L, vec.astype(np.float64), rdY1 + rdY2)
+    close("dvec", host(dv1) + host(dv2), dvec_ref)
+    # padded edges (zero weight) contribute no weight gradient to the model: w is masked
+    assert not host(T(w1, dev))[wb["mask"] == 0].any()
+    assert math.isfinite(float(host(h2).sum()))
