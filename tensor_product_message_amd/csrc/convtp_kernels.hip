@@ -42,7 +42,11 @@ template <> __device__ __forceinline__ const SlotDev* slot_tab<2>() { return kSl
 template <> __device__ __forceinline__ const SlotDev* slot_tab<3>() { return kSlot3.s; }
 __device__ __forceinline__ const ShTab& sh_tab() { return kShTab; }
 
-constexpr int kMaxThreads = 256;
+constexpr int kMaxThreads = 256;     // forward workgroups
+constexpr int kBwdMaxThreads = 512;  // backward: all channels of one sender
+#ifndef BWD_WPE
+#define BWD_WPE 3
+#endif
 
 // ------------------------------------------------------------ per-edge building blocks
 
@@ -121,13 +125,14 @@ __device__ __forceinline__ void edge_forward(float (&acc)[S::D3][CPL], const flo
 template <class S, int CPL>
 __device__ __forceinline__ void load_edge_operands(float (&xv)[S::D1][CPL], float (&wv)[S::P][CPL],
                                                    const float* __restrict__ x, const float* __restrict__ w,
-                                                   long j, long e, int C, int c) {
-    const float* xr = x + j * S::D1 * C + c;
-    const float* wr = w + e * S::P * C + c;
+                                                   long j, long e, int C, uint32_t voff) {
+    const rsrc_t xr = make_row(x + j * S::D1 * C, (long)S::D1 * C);
+    const rsrc_t wr = make_row(w + e * S::P * C, (long)S::P * C);
+    const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
 #pragma unroll
-    for (int d = 0; d < S::D1; ++d) load_ch<CPL>(xr + (long)d * C, xv[d]);
+    for (int d = 0; d < S::D1; ++d) bload<CPL>(xr, voff, (uint32_t)d * c4, xv[d]);
 #pragma unroll
-    for (int p = 0; p < S::P; ++p) load_ch<CPL>(wr + (long)p * C, wv[p]);
+    for (int p = 0; p < S::P; ++p) bload<CPL>(wr, voff, (uint32_t)p * c4, wv[p]);
 }
 
 // ------------------------------------------------------------ K1: CSR forward (deterministic)
@@ -143,9 +148,9 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
 
     const int i = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
-    const int c0 = (blockIdx.y * nth + tid) * CPL;
-    const bool active = c0 < C;
-    const int cl = active ? c0 : 0;
+    // lane owns channels c0 + 64 c, c < CPL (a wave covers 64 * CPL channels)
+    const int c0 = blockIdx.y * nth * CPL + (tid >> 6) * 64 * CPL + (tid & 63);
+    const uint32_t voff = opaque_lane(c0 < C ? (uint32_t)c0 * 4u : kOffLane);
 
     float acc[D3][CPL];
 #pragma unroll
@@ -157,18 +162,16 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
     for (int e = e0; e < e1; ++e) {
         const int buf = (e - e0) & 1;
         float xv[S::D1][CPL], wv[S::P][CPL];
-        load_edge_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, cl);
+        load_edge_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, voff);
         stage_sh<D2, VEC>(sY[buf], yv, e, tid);
         __syncthreads();
         build_T<L>(sT[buf], sY[buf], tid, nth);
         __syncthreads();
         edge_forward<S, CPL>(acc, xv, wv, sT[buf]);
     }
-    if (active) {
-        float* o = out + (long)i * D3 * C + c0;
+    const rsrc_t orow = make_row(out + (long)i * D3 * C, (long)D3 * C);
 #pragma unroll
-        for (int d = 0; d < D3; ++d) store_ch<CPL>(o + (long)d * C, acc[d]);
-    }
+    for (int d = 0; d < D3; ++d) bstore<CPL>(orow, voff, (uint32_t)(d * C * 4), acc[d]);
 }
 
 // ------------------------------------------------------------ K2: edge-parallel atomic forward (comparison)
@@ -191,9 +194,9 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
 
     const long e = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
-    const int c0 = (blockIdx.y * nth + tid) * CPL;
+    const int c0 = blockIdx.y * nth * CPL + (tid >> 6) * 64 * CPL + (tid & 63);
     const bool active = c0 < C;
-    const int cl = active ? c0 : 0;
+    const uint32_t voff = opaque_lane(active ? (uint32_t)c0 * 4u : kOffLane);
 
     // receiver of edge e: last i with row_ptr[i] <= e
     int lo = 0, hi = n_nodes;
@@ -204,7 +207,7 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
     const int i = lo;
 
     float xv[S::D1][CPL], wv[S::P][CPL];
-    load_edge_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, cl);
+    load_edge_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, voff);
     stage_sh<D2, VEC>(sY, yv, e, tid);
     __syncthreads();
     build_T<L>(sT, sY, tid, nth);
@@ -220,7 +223,7 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
 #pragma unroll
         for (int d = 0; d < D3; ++d)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + c, acc[d][c]);
+            for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + 64 * c, acc[d][c]);
     }
 }
 
@@ -235,7 +238,7 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
 // With VEC, dvec[e] = J(vec_e)^T dY[e] instead of dY.
 
 template <int L, int CPL, bool VEC>
-__global__ void __launch_bounds__(kMaxThreads)
+__global__ void __launch_bounds__(kBwdMaxThreads) __attribute__((amdgpu_waves_per_eu(BWD_WPE, 8)))
 k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ yv,
              const float* __restrict__ w, const int* __restrict__ send_ptr, const int* __restrict__ send_perm,
              const int* __restrict__ send_recv, float* __restrict__ dx, float* __restrict__ dw,
@@ -244,26 +247,22 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
     constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NTP = (S::NT + 3) & ~3;
     __shared__ float sT[2][NTP];
     __shared__ float sY[2][16];
-    __shared__ float sRed[2][kMaxThreads / 64][16];
+    __shared__ float sRed[2][kBwdMaxThreads / 64][16];
 
     const int j = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nth >> 6;
     const int c0 = tid * CPL;
-    const bool active = c0 < C;
-    const int cl = active ? c0 : 0;
+    const uint32_t voff = opaque_lane(c0 < C ? (uint32_t)c0 * 4u : kOffLane);   // no channel: loads 0, stores dropped
 
     float xv[D1][CPL], dxa[D1][CPL];
     {
-        const float* xr = x + (long)j * D1 * C + cl;
+        const rsrc_t xr = make_row(x + (long)j * D1 * C, (long)D1 * C);
 #pragma unroll
         for (int d = 0; d < D1; ++d) {
-            load_ch<CPL>(xr + (long)d * C, xv[d]);
+            bload<CPL>(xr, voff, (uint32_t)(d * C * 4), xv[d]);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                xv[d][c] = active ? xv[d][c] : 0.0f;
-                dxa[d][c] = 0.0f;
-            }
+            for (int c = 0; c < CPL; ++c) dxa[d][c] = 0.0f;
         }
     }
 
@@ -274,12 +273,13 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
         const long i = send_recv[k];
         float gv[D3][CPL], wv[P][CPL];
         {
-            const float* gr = G + i * D3 * C + cl;
-            const float* wr = w + e * P * C + cl;
+            const rsrc_t gr = make_row(G + i * D3 * C, (long)D3 * C);
+            const rsrc_t wr = make_row(w + e * P * C, (long)P * C);
+            const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
 #pragma unroll
-            for (int d = 0; d < D3; ++d) load_ch<CPL>(gr + (long)d * C, gv[d]);
+            for (int d = 0; d < D3; ++d) bload<CPL>(gr, voff, (uint32_t)d * c4, gv[d]);
 #pragma unroll
-            for (int p = 0; p < P; ++p) load_ch<CPL>(wr + (long)p * C, wv[p]);
+            for (int p = 0; p < P; ++p) bload<CPL>(wr, voff, (uint32_t)p * c4, wv[p]);
         }
         stage_sh<D2, VEC>(sY[buf], yv, e, tid);
         __syncthreads();
@@ -287,42 +287,11 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
         __syncthreads();
         const float* T = sT[buf];
 
-        // dx and dw through v_p = T_p^T g
-        float* dwr = dw + e * P * C + c0;
-        static_for<P>([&](auto pI) __attribute__((always_inline)) {
-            constexpr int p = decltype(pI)::value;
-            constexpr PathL q = S::paths[p];
-            constexpr int n1 = 2 * q.l1 + 1;
-            constexpr int o1 = q.l1 * q.l1, o3 = q.l3 * q.l3;
-            constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
-            float v[n1][CPL];
-            static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
-                constexpr int t = t0 + decltype(tI)::value;
-                constexpr TSlot s = S::slots[t];
-                const float tv = T[t];
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    if constexpr (first_m1<S>(t))
-                        v[s.m1][c] = tv * gv[o3 + s.m3][c];
-                    else
-                        v[s.m1][c] = __builtin_fmaf(tv, gv[o3 + s.m3][c], v[s.m1][c]);
-                }
-            });
-            float dwv[CPL];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                dwv[c] = xv[o1][c] * v[0][c];
-#pragma unroll
-                for (int a = 1; a < n1; ++a) dwv[c] = __builtin_fmaf(xv[o1 + a][c], v[a][c], dwv[c]);
-            }
-            if (active) store_ch<CPL>(dwr + (long)p * C, dwv);
-#pragma unroll
-            for (int a = 0; a < n1; ++a)
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) dxa[o1 + a][c] = __builtin_fmaf(wv[p][c], v[a][c], dxa[o1 + a][c]);
-        });
-
-        // dY: per-lane partial sums over this lane's channels, path by path
+        // Work grouped by (l1, l3): for each pair, v_p, dw_p and dx for its
+        // paths, then B_p from the products x[l1 m1] g[l3 m3] formed m1 by m1
+        // and shared by the pair's paths.  A scheduling barrier after each
+        // pair bounds register lifetimes.
+        const rsrc_t dwr = make_row(dw + e * P * C, (long)P * C);
         float dya[D2];
 #pragma unroll
         for (int d = 0; d < D2; ++d) dya[d] = 0.0f;
@@ -330,38 +299,84 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
             constexpr int l1 = decltype(l1I)::value;
             static_for<L + 1>([&](auto l3I) __attribute__((always_inline)) {
                 constexpr int l3 = decltype(l3I)::value;
-                constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
-                float xg[n1][n3][CPL];
-#pragma unroll
-                for (int a = 0; a < n1; ++a)
-#pragma unroll
-                    for (int b = 0; b < n3; ++b)
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) xg[a][b][c] = xv[l1 * l1 + a][c] * gv[l3 * l3 + b][c];
-                static_for<P>([&](auto pI) __attribute__((always_inline)) {
-                    constexpr int p = decltype(pI)::value;
-                    constexpr PathL q = S::paths[p];
-                    if constexpr (q.l1 == l1 && q.l3 == l3) {
-                        constexpr int n2 = 2 * q.l2 + 1, o2 = q.l2 * q.l2;
-                        constexpr int z0 = nz_begin<S>(p), z1 = nz_begin<S>(p + 1);
-                        float B[n2][CPL];
-                        static_for<z1 - z0>([&](auto zI) __attribute__((always_inline)) {
-                            constexpr int n = z0 + decltype(zI)::value;
-                            constexpr CgNz nzv = S::nz[n];
+                constexpr PairPaths pp = pair_paths<S>(l1, l3);
+                if constexpr (pp.n > 0) {
+                    constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
+                    constexpr int o1 = l1 * l1, o3 = l3 * l3;
+                    // (a) v_p = T_p^T g, dw_p = x . v_p, dx += w_p v_p
+                    static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+                        constexpr int p = pp.p[decltype(kI)::value];
+                        constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
+                        float v[n1][CPL];
+                        static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
+                            constexpr int t = t0 + decltype(tI)::value;
+                            constexpr TSlot s = S::slots[t];
+                            const float tv = T[t];
 #pragma unroll
                             for (int c = 0; c < CPL; ++c) {
-                                if constexpr (nz_first_m2<S>(n))
-                                    B[nzv.m2][c] = nzv.c * xg[nzv.m1][nzv.m3][c];
+                                if constexpr (first_m1<S>(t))
+                                    v[s.m1][c] = tv * gv[o3 + s.m3][c];
                                 else
-                                    B[nzv.m2][c] = __builtin_fmaf(nzv.c, xg[nzv.m1][nzv.m3][c], B[nzv.m2][c]);
+                                    v[s.m1][c] = __builtin_fmaf(tv, gv[o3 + s.m3][c], v[s.m1][c]);
                             }
                         });
+                        float dwv[CPL];
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) {
+                            dwv[c] = xv[o1][c] * v[0][c];
+#pragma unroll
+                            for (int a = 1; a < n1; ++a) dwv[c] = __builtin_fmaf(xv[o1 + a][c], v[a][c], dwv[c]);
+                        }
+                        bstore<CPL>(dwr, voff, (uint32_t)p * opaque_u32((uint32_t)C * 4u), dwv);
+#pragma unroll
+                        for (int a = 0; a < n1; ++a)
+#pragma unroll
+                            for (int c = 0; c < CPL; ++c) {
+                                dxa[o1 + a][c] = __builtin_fmaf(wv[p][c], v[a][c], dxa[o1 + a][c]);
+                                pin_f32(dxa[o1 + a][c]);
+                            }
+                        if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
+                    // (b) B_p[m2] = sum C_p[m1][m2][m3] x[m1] g[m3], m1 outermost
+                    float B[kMaxL + 1][2 * kMaxL + 1][CPL];
+                    static_for<n1>([&](auto aI) __attribute__((always_inline)) {
+                        constexpr int a = decltype(aI)::value;
+                        float p3[n3][CPL];
+#pragma unroll
+                        for (int b = 0; b < n3; ++b)
+#pragma unroll
+                            for (int c = 0; c < CPL; ++c) p3[b][c] = xv[o1 + a][c] * gv[o3 + b][c];
+                        static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+                            constexpr int k = decltype(kI)::value;
+                            constexpr int p = pp.p[k];
+                            constexpr int z0 = nz_m1_begin<S>(p, a), z1 = nz_m1_begin<S>(p, a + 1);
+                            static_for<z1 - z0>([&](auto zI) __attribute__((always_inline)) {
+                                constexpr int n = z0 + decltype(zI)::value;
+                                constexpr CgNz nzv = S::nz[n];
+#pragma unroll
+                                for (int c = 0; c < CPL; ++c) {
+                                    if constexpr (nz_first_m2<S>(n))
+                                        B[k][nzv.m2][c] = nzv.c * p3[nzv.m3][c];
+                                    else
+                                        B[k][nzv.m2][c] = __builtin_fmaf(nzv.c, p3[nzv.m3][c], B[k][nzv.m2][c]);
+                                }
+                            });
+                        });
+                        if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+                    });
+                    // (c) dY partial sums
+                    static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+                        constexpr int k = decltype(kI)::value;
+                        constexpr int p = pp.p[k];
+                        constexpr int n2 = 2 * S::paths[p].l2 + 1, o2 = S::paths[p].l2 * S::paths[p].l2;
 #pragma unroll
                         for (int b = 0; b < n2; ++b)
 #pragma unroll
-                            for (int c = 0; c < CPL; ++c) dya[o2 + b] = __builtin_fmaf(wv[p][c], B[b][c], dya[o2 + b]);
-                    }
-                });
+                            for (int c = 0; c < CPL; ++c) dya[o2 + b] = __builtin_fmaf(wv[p][c], B[k][b][c], dya[o2 + b]);
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             });
         });
 
@@ -409,11 +424,9 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
         }
     }
 
-    if (active) {
-        float* o = dx + (long)j * D1 * C + c0;
+    const rsrc_t dxr = make_row(dx + (long)j * D1 * C, (long)D1 * C);
 #pragma unroll
-        for (int d = 0; d < D1; ++d) store_ch<CPL>(o + (long)d * C, dxa[d]);
-    }
+    for (int d = 0; d < D1; ++d) bstore<CPL>(dxr, voff, (uint32_t)(d * C * 4), dxa[d]);
 }
 
 // ------------------------------------------------------------ standalone harmonics (vec -> Y, dY -> dvec)
@@ -505,6 +518,7 @@ hipError_t fwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
 
 template <int L, int CPL>
 hipError_t bwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
+    static_assert(CPL == 1, "the backward maps one channel per lane");
     dim3 grid(a.n_nodes), block(64 * m.waves);
     if (a.vec_mode)
         hipLaunchKernelGGL((k_bwd_sender<L, CPL, true>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
@@ -521,18 +535,24 @@ hipError_t fwd_L(const LaunchArgs& a, hipStream_t st) {
     return m.cpl == 2 ? fwd_dispatch<L, 2>(a, m, st) : fwd_dispatch<L, 1>(a, m, st);
 }
 
+ChanMap bwd_chan_map(int C) {
+    ChanMap m{};
+    m.cpl = 1;
+    m.waves = (C + 63) / 64;
+    m.tiles = 1;
+    return m;
+}
+
 template <int L>
 hipError_t bwd_L(const LaunchArgs& a, hipStream_t st) {
-    const ChanMap m = chan_map(a.C, kMaxThreads / 64);
-    return m.cpl == 2 ? bwd_dispatch<L, 2>(a, m, st) : bwd_dispatch<L, 1>(a, m, st);
+    return bwd_dispatch<L, 1>(a, bwd_chan_map(a.C), st);
 }
 
 }  // namespace
 
 bool bwd_supports_channels(int C) {
     // the backward keeps all channels of a sender in one workgroup (deterministic dY)
-    const ChanMap m = chan_map(C, 1 << 20);
-    return m.waves <= kMaxThreads / 64;
+    return bwd_chan_map(C).waves <= kBwdMaxThreads / 64;
 }
 
 hipError_t launch_fwd(const LaunchArgs& a, hipStream_t st) {

@@ -55,6 +55,27 @@ constexpr bool nz_first_m2(int n) {
     return true;
 }
 
+// First non-zero of path p with m1 >= a (non-zeros are sorted by m1, m2, m3).
+template <class S>
+constexpr int nz_m1_begin(int p, int a) {
+    for (int n = nz_begin<S>(p); n < nz_begin<S>(p + 1); ++n)
+        if (S::nz[n].m1 >= a) return n;
+    return nz_begin<S>(p + 1);
+}
+
+// Paths sharing (l1, l3), in path order (at most kMaxL + 1 of them).
+struct PairPaths {
+    int n;
+    int p[kMaxL + 1];
+};
+template <class S>
+constexpr PairPaths pair_paths(int l1, int l3) {
+    PairPaths r{0, {0, 0, 0, 0}};
+    for (int p = 0; p < S::P; ++p)
+        if (S::paths[p].l1 == l1 && S::paths[p].l3 == l3) r.p[r.n++] = p;
+    return r;
+}
+
 // ------------------------------------------------------------ slot tables in device memory
 
 // Lane-parallel build of T_p[m1][m3] = c1 * Y[y1] + c2 * Y[y2]; y1 | (y2 << 8).
@@ -212,6 +233,61 @@ __device__ __forceinline__ float wave_sum_to_last(float v) {
 
 __device__ __forceinline__ float lane_value(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ------------------------------------------------------------ buffer rows
+//
+// Every feature/weight row is addressed through a buffer resource built from
+// a wave-uniform base (SGPRs), one per-lane byte offset (a single VGPR) and a
+// per-path/component offset in an SGPR.  Lanes with no channel get an offset
+// beyond the row: their loads return 0 and their stores are dropped by the
+// buffer range check.
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kSrdWord3 = 0x00020000;      // gfx9 raw buffer, 32-bit dwords
+constexpr uint32_t kOffLane = 0x80000000u;       // out-of-range lane offset
+
+__device__ __forceinline__ rsrc_t make_row(const float* base, long n_floats) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)(n_floats * 4),
+                                             (int)kSrdWord3);
+}
+
+// A uniform value the compiler must treat as redefined here: offsets built
+// from it are formed next to their use instead of being hoisted out of the
+// edge loop (dozens of hoisted per-path offsets exhaust the SGPRs).
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+// Per-lane byte offset made opaque, so "+4 per channel" folds into the
+// instruction's immediate offset and adjacent channels merge into one
+// dwordx2 access (a select hidden behind the offset would block that).
+__device__ __forceinline__ uint32_t opaque_lane(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Pins a register value at this point of the program: the update that
+// produced it cannot be sunk past later stores (keeps per-path temporaries
+// short-lived instead of deferring every accumulation to the loop latch).
+__device__ __forceinline__ void pin_f32(float& v) { asm volatile("" : "+v"(v)); }
+
+// A lane owns channels c0 + 64 * c (c < CPL): every access instruction then
+// covers 64 consecutive floats (256 contiguous bytes), and channel c's extra
+// 256 bytes go into the scalar offset.
+template <int CPL>
+__device__ __forceinline__ void bload(rsrc_t r, uint32_t voff, uint32_t soff, float (&v)[CPL]) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+        v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff + 256u * c, 0));
+}
+
+template <int CPL>
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t voff, uint32_t soff, const float (&v)[CPL]) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v[c]), r, voff, soff + 256u * c, 0);
 }
 
 // ------------------------------------------------------------ vector loads
