@@ -204,8 +204,22 @@ def workload_tiny(ctp, torch, dev, args):
                 edges=d["n_edges"], cfg=cfg, cpu=None)
 
 
+def workload_copy(ctp, torch, dev, args):
+    """Calibration only: a plain 1 GiB device-to-device copy (reads 1 GiB,
+    writes 1 GiB), used to scale the HBM byte counters of the profiler."""
+    n = (1 << 30) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+
+    def step(t):
+        t.run("copy", lambda: dst.copy_(src))
+
+    return dict(step=step, kernel_bytes={"copy": 2 * 4 * n}, dominant="copy", edges=0,
+                cfg={"workload": "calibration: 1 GiB fp32 device copy"}, cpu=None)
+
+
 WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
-             "water": workload_water, "tiny": workload_tiny}
+             "water": workload_water, "tiny": workload_tiny, "copy": workload_copy}
 
 
 # ------------------------------------------------------------ CPU baseline (oracle)
@@ -335,7 +349,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": wl["cfg"],
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-        "edges_per_s": round(wl["edges"] / (ms_value * 1e-3), 1),
+        "edges_per_s": round(wl["edges"] / (ms_value * 1e-3), 1) if wl["edges"] else None,
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},

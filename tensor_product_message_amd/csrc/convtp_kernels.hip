@@ -44,6 +44,9 @@ __device__ __forceinline__ const ShTab& sh_tab() { return kShTab; }
 
 constexpr int kMaxThreads = 256;     // forward workgroups
 constexpr int kBwdMaxThreads = 512;  // backward: all channels of one sender
+#ifndef FWD_WPE
+#define FWD_WPE 1
+#endif
 #ifndef BWD_WPE
 #define BWD_WPE 3
 #endif
@@ -136,15 +139,111 @@ __device__ __forceinline__ void load_edge_operands(float (&xv)[S::D1][CPL], floa
 }
 
 // ------------------------------------------------------------ K1: CSR forward (deterministic)
+//
+// Rotating prefetch: right after path p of edge e has consumed w[e, p], the
+// same registers receive w[e+1, p]; each x block is refilled with the next
+// sender's row after its last use.  Every load thus has about one edge of
+// arithmetic to arrive, with no second register set.  The next edge's Y is
+// loaded early and its T is built into the other LDS buffer after compute.
+
+template <class S>
+constexpr bool last_path_of_l1(int p) {
+    return p + 1 == S::P || S::paths[p + 1].l1 != S::paths[p].l1;
+}
+
+// Path loop of one edge with refills for the next edge.
+template <class S, int CPL>
+__device__ __forceinline__ void edge_forward_refill(float (&acc)[S::D3][CPL], float (&xv)[S::D1][CPL],
+                                                    float (&wv)[S::P][CPL], const float* sT, rsrc_t nx,
+                                                    rsrc_t nw, uint32_t nvoff, int C) {
+    static_for<S::P>([&](auto pI) __attribute__((always_inline)) {
+        constexpr int p = decltype(pI)::value;
+        constexpr PathL q = S::paths[p];
+        constexpr int n1 = 2 * q.l1 + 1, n3 = 2 * q.l3 + 1;
+        constexpr int o1 = q.l1 * q.l1, o3 = q.l3 * q.l3;
+        constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
+        if constexpr (n1 <= n3) {
+            float xs[n1][CPL];
+#pragma unroll
+            for (int a = 0; a < n1; ++a)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) xs[a][c] = wv[p][c] * xv[o1 + a][c];
+            static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
+                constexpr int t = t0 + decltype(tI)::value;
+                constexpr TSlot s = S::slots[t];
+                const float tv = sT[t];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    acc[o3 + s.m3][c] = __builtin_fmaf(tv, xs[s.m1][c], acc[o3 + s.m3][c]);
+            });
+        } else {
+            float u[n3][CPL];
+            static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
+                constexpr int t = t0 + decltype(tI)::value;
+                constexpr TSlot s = S::slots[t];
+                const float tv = sT[t];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    if constexpr (first_m3<S>(t))
+                        u[s.m3][c] = tv * xv[o1 + s.m1][c];
+                    else
+                        u[s.m3][c] = __builtin_fmaf(tv, xv[o1 + s.m1][c], u[s.m3][c]);
+                }
+            });
+#pragma unroll
+            for (int k = 0; k < n3; ++k)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[o3 + k][c] = __builtin_fmaf(wv[p][c], u[k][c], acc[o3 + k][c]);
+        }
+        // keep this path's arithmetic here (pure code would otherwise sink to the loop latch)
+#pragma unroll
+        for (int k = 0; k < n3; ++k)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) pin_f32(acc[o3 + k][c]);
+        // refills for the next edge (loads return 0 when there is none)
+        const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+        bload<CPL>(nw, nvoff, (uint32_t)p * c4, wv[p]);
+        if constexpr (last_path_of_l1<S>(p)) {
+#pragma unroll
+            for (int a = 0; a < n1; ++a) bload<CPL>(nx, nvoff, (uint32_t)(o1 + a) * c4, xv[o1 + a]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// Component tid of Y for edge e (lanes >= D2 return 0).
+template <int D2, bool VEC>
+__device__ __forceinline__ float sh_value(const float* __restrict__ yv, long e, int tid) {
+    float r = 0.0f;
+    if (tid < D2) {
+        if constexpr (VEC) {
+            const float* v = yv + 3 * e;
+            r = sh_component(tid, v[0], v[1], v[2]);
+        } else {
+            r = yv[e * D2 + tid];
+        }
+    }
+    return r;
+}
+
+template <int L>
+__device__ __forceinline__ void build_T_lds(float* sT, const float* sY, const SlotDev* tab, int tid, int nth) {
+    constexpr int NT = Spec<L, L, L>::NT;
+    for (int t = tid; t < NT; t += nth) {
+        const SlotDev s = tab[t];
+        sT[t] = s.c1 * sY[s.yy & 0xff] + s.c2 * sY[s.yy >> 8];
+    }
+}
 
 template <int L, int CPL, bool VEC>
-__global__ void __launch_bounds__(kMaxThreads)
+__global__ void __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(FWD_WPE, 8)))
 k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, const float* __restrict__ w,
           const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ out) {
     using S = Spec<L, L, L>;
-    constexpr int D2 = S::D2, D3 = S::D3, NTP = (S::NT + 3) & ~3;
+    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
     __shared__ float sT[2][NTP];
     __shared__ float sY[2][16];
+    __shared__ SlotDev sTab[NT];
 
     const int i = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
@@ -159,15 +258,35 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
         for (int c = 0; c < CPL; ++c) acc[d][c] = 0.0f;
 
     const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
-    for (int e = e0; e < e1; ++e) {
-        const int buf = (e - e0) & 1;
-        float xv[S::D1][CPL], wv[S::P][CPL];
-        load_edge_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, voff);
-        stage_sh<D2, VEC>(sY[buf], yv, e, tid);
+    if (e0 < e1) {
+        {
+            const SlotDev* tab = slot_tab<L>();
+            for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
+        }
+        float xv[D1][CPL], wv[P][CPL];
+        load_edge_operands<S, CPL>(xv, wv, x, w, senders[e0], e0, C, voff);
+        const float y0 = sh_value<D2, VEC>(yv, e0, tid);
+        if (tid < D2) sY[0][tid] = y0;
         __syncthreads();
-        build_T<L>(sT[buf], sY[buf], tid, nth);
+        build_T_lds<L>(sT[0], sY[0], sTab, tid, nth);
         __syncthreads();
-        edge_forward<S, CPL>(acc, xv, wv, sT[buf]);
+        for (int e = e0; e < e1; ++e) {
+            const int buf = (e - e0) & 1;
+            const bool has_next = e + 1 < e1;
+            const long en = has_next ? e + 1 : e;
+            const long jn = senders[en];
+            const rsrc_t nx = make_row(x + jn * D1 * C, (long)D1 * C);
+            const rsrc_t nw = make_row(w + en * P * C, (long)P * C);
+            const uint32_t nvoff = has_next ? voff : kOffLane;
+            const float ynext = sh_value<D2, VEC>(yv, en, tid);
+            edge_forward_refill<S, CPL>(acc, xv, wv, sT[buf], nx, nw, nvoff, C);
+            if (has_next) {
+                if (tid < D2) sY[buf ^ 1][tid] = ynext;
+                __syncthreads();
+                build_T_lds<L>(sT[buf ^ 1], sY[buf ^ 1], sTab, tid, nth);
+                __syncthreads();
+            }
+        }
     }
     const rsrc_t orow = make_row(out + (long)i * D3 * C, (long)D3 * C);
 #pragma unroll

@@ -152,25 +152,13 @@ constexpr ShTab make_sh_tab() {
 
 __device__ __forceinline__ const ShTab& sh_tab();
 
-// Powers w^a = (x + iy)^a for a = 0..3 as (cos-part, sin-part).
-struct XyPow {
-    float c[4], s[4];
-};
-__device__ __forceinline__ XyPow xy_powers(float x, float y) {
-    XyPow p;
-    p.c[0] = 1.0f; p.s[0] = 0.0f;
-    p.c[1] = x;    p.s[1] = y;
-    p.c[2] = x * x - y * y;          p.s[2] = 2.0f * x * y;
-    p.c[3] = p.c[2] * x - p.s[2] * y; p.s[3] = p.c[2] * y + p.s[2] * x;
-    return p;
-}
-
-__device__ __forceinline__ float pick4(const float* v, int a) {
-    float r = v[0];
-    r = (a == 1) ? v[1] : r;
-    r = (a == 2) ? v[2] : r;
-    r = (a == 3) ? v[3] : r;
-    return r;
+// Re and Im of (x + iy)^a, a = 0..3, selected with scalar selects (no
+// dynamically indexed local arrays, which the compiler would move to LDS).
+__device__ __forceinline__ void xy_power(float x, float y, int a, float& re, float& im) {
+    const float c2 = x * x - y * y, s2 = 2.0f * x * y;
+    const float c3 = c2 * x - s2 * y, s3 = c2 * y + s2 * x;
+    re = a == 0 ? 1.0f : (a == 1 ? x : (a == 2 ? c2 : c3));
+    im = a == 0 ? 0.0f : (a == 1 ? y : (a == 2 ? s2 : s3));
 }
 
 __device__ __forceinline__ float horner4(const float* q, float z) {
@@ -184,29 +172,29 @@ __device__ __forceinline__ float sh_component(int k, float vx, float vy, float v
     const float inv = 1.0f / sqrtf(n2);
     const float x = vx * inv, y = vy * inv, z = vz * inv;
     const ShCoef& c = sh_tab().k[k];
-    const XyPow p = xy_powers(x, y);
-    const float A = c.sine ? pick4(p.s, c.a) : pick4(p.c, c.a);
-    return A * horner4(c.q, z);
+    float re, im;
+    xy_power(x, y, c.a, re, im);
+    return (c.sine ? im : re) * horner4(c.q, z);
 }
 
 // dY_k / dr (gradient of the polynomial form at the unit vector r).
 __device__ __forceinline__ void sh_component_grad(int k, float x, float y, float z, float g[3]) {
     const ShCoef& c = sh_tab().k[k];
-    const XyPow p = xy_powers(x, y);
     const float Q = horner4(c.q, z), dQ = horner4(c.dq, z);
     const int a = c.a;
     const float fa = static_cast<float>(a);
-    const int am1 = a > 0 ? a - 1 : 0;
-    const float cm = pick4(p.c, am1), sm = pick4(p.s, am1);
+    float re, im, rm, imm;
+    xy_power(x, y, a, re, im);
+    xy_power(x, y, a > 0 ? a - 1 : 0, rm, imm);
     float A, dAx, dAy;
-    if (c.sine) {
-        A = pick4(p.s, a);
-        dAx = fa * sm;
-        dAy = fa * cm;
-    } else {
-        A = pick4(p.c, a);
-        dAx = fa * cm;
-        dAy = -fa * sm;
+    if (c.sine) {          // Im (x+iy)^a:  d/dx = a Im w^(a-1),  d/dy = a Re w^(a-1)
+        A = im;
+        dAx = fa * imm;
+        dAy = fa * rm;
+    } else {               // Re (x+iy)^a:  d/dx = a Re w^(a-1),  d/dy = -a Im w^(a-1)
+        A = re;
+        dAx = fa * rm;
+        dAy = -fa * imm;
     }
     g[0] = dAx * Q;
     g[1] = dAy * Q;
