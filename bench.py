@@ -40,13 +40,16 @@ def bwd_bytes(N, E, C, D1, D2, D3, P, S):
     return 4 * (2 * E * P * C + 2 * E * S + 2 * E + (N + 1) + 2 * N * C * D1 + N * C * D3)
 
 
+KERNEL_SOURCES = ("convtp_kernels.hip", "device_common.hpp", "tables.hpp", "kernels.hpp")
+
+
 def kernel_sources_sha():
+    """Hash of the sources the conv TP kernels are compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_product_message_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -236,7 +239,7 @@ def cpu_baseline(spec, sample_nodes):
     d, L, shp, fb = spec["d"], spec["L"], spec["shp"], spec["fb"]
     N, E = shp[0], shp[1]
     rp, s = d["row_ptr"], d["senders"]
-    rows = np.arange(min(sample_nodes, N))
+    rows = np.arange(min(sample_nodes, N) if sample_nodes > 0 else N)
     e_lo, e_hi = 0, int(rp[rows[-1] + 1])
     Y = osh.real_sh(L, d["vec"][e_lo:e_hi].astype(np.float64))
     x = d["x"].cpu().numpy()
@@ -272,7 +275,7 @@ def cpu_baseline(spec, sample_nodes):
             "edges_per_s": round(edges_per_s, 1), "seconds": round(t, 2),
             "sample": f"{what} over the {e_sample} in-edges of the first {len(rows)} receivers "
                       f"({e_sample / E:.1%} of the edges), fp64 C edge loop, {nt} OpenMP threads; "
-                      "GB/s scaled by the full step's bytes per edge"}
+                      "GB/s = edges/s x the step's algorithmic bytes per edge"}
 
 
 # ------------------------------------------------------------ traffic from committed counters
@@ -298,7 +301,8 @@ def main():
     ap.add_argument("--channels", type=int, default=128, help="sweepC only")
     ap.add_argument("--vec", action="store_true", help="l3fb with edge vectors instead of Y")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-nodes", type=int, default=2048)
+    ap.add_argument("--cpu-sample-nodes", type=int, default=0,
+                    help="receivers in the CPU-oracle sample (0: all of them)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the conv TP path here is "

@@ -112,9 +112,9 @@ int32_t conv_tp_fwd(const conv_tp_problem *prob, const float *x, const float *y_
 
 /* Backward for upstream gradient grad_out = dL/dout: writes dx, dw and dY
  * (y_mode 0) or dvec = (dY/dvec)^T dY (y_mode 1).  One workgroup per sender
- * walks its out-edges through (send_ptr, send_perm, send_recv).  algo must
- * be 0; channels must fit one workgroup (C <= 512 when C % 128 == 0, else
- * C <= 256). */
+ * walks its out-edges through (send_ptr, send_perm, send_recv), one channel
+ * per lane, so every channel of a sender is in one workgroup and dY is summed
+ * in a fixed order.  algo must be 0; C <= 512. */
 int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y_or_vec,
                     const float *w, const int32_t *row_ptr, const int32_t *senders, const int32_t *send_ptr,
                     const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec,

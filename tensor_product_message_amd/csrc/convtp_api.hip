@@ -185,7 +185,7 @@ int32_t conv_tp_bwd(const conv_tp_problem* prob, const float* grad_out, const fl
     if (int r = check_problem(prob, &s)) return r;
     if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the backward has only the deterministic algorithm (algo 0)");
     if (!ctp::bwd_supports_channels(prob->channels))
-        return fail(CTP_EUNSUPPORTED, "backward needs C <= 512 (C %% 128 == 0) or C <= 256, got %d", prob->channels);
+        return fail(CTP_EUNSUPPORTED, "backward needs C <= 512, got %d", prob->channels);
     if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
     if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
     if (int r = need(y_or_vec, s.E * s.S, 4, "y_or_vec")) return r;

@@ -102,7 +102,7 @@ def test_fwd_rejects_bad_pointers(capi):
 def test_bwd_rejections(capi):
     assert _bwd(capi, _prob(capi, algo=1)) == capi.CTP_EUNSUPPORTED
     assert _bwd(capi, _prob(capi, channels=1024)) == capi.CTP_EUNSUPPORTED
-    assert _bwd(capi, _prob(capi, channels=320)) == capi.CTP_EUNSUPPORTED
+    assert _bwd(capi, _prob(capi, channels=513)) == capi.CTP_EUNSUPPORTED
     p = _prob(capi)
     for k in ("g", "x", "y", "w", "rp", "s", "sp", "pe", "sr", "dx", "dw", "dy"):
         assert _bwd(capi, p, **{k: NUL}) == capi.CTP_EINVAL, k

@@ -110,7 +110,7 @@ SMALL = [  # (N, C, L): several channel tiles, ragged lane tails, every degree
 @pytest.mark.parametrize("y_mode", [0, 1])
 def test_small_poisson(ctp, dev, n, c, L, y_mode):
     d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=n + c + L)
-    bwd_ok = (c % 128 == 0 and c <= 512) or c <= 256
+    bwd_ok = c <= 512
     run_small(ctp, dev, d, L, y_mode, 0, bwd=bwd_ok)
     run_small(ctp, dev, d, L, y_mode, 1, bwd=False)
 
