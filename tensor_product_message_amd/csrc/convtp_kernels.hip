@@ -226,6 +226,17 @@ __device__ __forceinline__ float sh_value(const float* __restrict__ yv, long e, 
     return r;
 }
 
+// The same through a buffer row in Y mode: lanes >= D2 read past the row and get 0.
+template <int D2, bool VEC>
+__device__ __forceinline__ float sh_load(const float* __restrict__ yv, long e, int tid) {
+    if constexpr (VEC) {
+        return sh_value<D2, true>(yv, e, tid);
+    } else {
+        const rsrc_t yr = make_row(yv + e * D2, D2);
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(yr, (uint32_t)tid * 4u, 0, 0));
+    }
+}
+
 template <int L>
 __device__ __forceinline__ void build_T_lds(float* sT, const float* sY, const SlotDev* tab, int tid, int nth) {
     constexpr int NT = Spec<L, L, L>::NT;
@@ -356,6 +367,20 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
 //   dY[e, l2 m2] = sum_c sum_p w_p B_p[m2]           (lanes, then waves, fixed order)
 // With VEC, dvec[e] = J(vec_e)^T dY[e] instead of dY.
 
+// G row of receiver i and w row of edge e, CPL channels per lane.
+template <class S, int CPL>
+__device__ __forceinline__ void load_bwd_operands(float (&gv)[S::D3][CPL], float (&wv)[S::P][CPL],
+                                                  const float* __restrict__ G, const float* __restrict__ w, long i,
+                                                  long e, int C, uint32_t voff) {
+    const rsrc_t gr = make_row(G + i * S::D3 * C, (long)S::D3 * C);
+    const rsrc_t wr = make_row(w + e * S::P * C, (long)S::P * C);
+    const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+#pragma unroll
+    for (int d = 0; d < S::D3; ++d) bload<CPL>(gr, voff, (uint32_t)d * c4, gv[d]);
+#pragma unroll
+    for (int p = 0; p < S::P; ++p) bload<CPL>(wr, voff, (uint32_t)p * c4, wv[p]);
+}
+
 template <int L, int CPL, bool VEC>
 __global__ void __launch_bounds__(kBwdMaxThreads) __attribute__((amdgpu_waves_per_eu(BWD_WPE, 8)))
 k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ yv,
@@ -363,14 +388,15 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
              const int* __restrict__ send_recv, float* __restrict__ dx, float* __restrict__ dw,
              float* __restrict__ dyv) {
     using S = Spec<L, L, L>;
-    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NTP = (S::NT + 3) & ~3;
+    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
     __shared__ float sT[2][NTP];
     __shared__ float sY[2][16];
-    __shared__ float sRed[2][kBwdMaxThreads / 64][16];
+    __shared__ float sRed[kBwdMaxThreads / 64][16];
+    __shared__ SlotDev sTab[NT];
 
     const int j = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6, nwaves = nth >> 6;
+    const int nwaves = nth >> 6;
     const int c0 = tid * CPL;
     const uint32_t voff = opaque_lane(c0 < C ? (uint32_t)c0 * 4u : kOffLane);   // no channel: loads 0, stores dropped
 
@@ -386,160 +412,178 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
     }
 
     const int k0 = send_ptr[j], k1 = send_ptr[j + 1];
-    for (int k = k0; k < k1; ++k) {
-        const int buf = (k - k0) & 1;
-        const long e = send_perm[k];
-        const long i = send_recv[k];
-        float gv[D3][CPL], wv[P][CPL];
+    if (k0 < k1) {
         {
-            const rsrc_t gr = make_row(G + i * D3 * C, (long)D3 * C);
-            const rsrc_t wr = make_row(w + e * P * C, (long)P * C);
-            const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
-#pragma unroll
-            for (int d = 0; d < D3; ++d) bload<CPL>(gr, voff, (uint32_t)d * c4, gv[d]);
-#pragma unroll
-            for (int p = 0; p < P; ++p) bload<CPL>(wr, voff, (uint32_t)p * c4, wv[p]);
+            const SlotDev* tab = slot_tab<L>();
+            for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
         }
-        stage_sh<D2, VEC>(sY[buf], yv, e, tid);
+        float gv[D3][CPL], wv[P][CPL];
+        long e = send_perm[k0];
+        const float y0 = sh_load<D2, VEC>(yv, e, tid);
+        load_bwd_operands<S, CPL>(gv, wv, G, w, send_recv[k0], e, C, voff);
+        if (tid < D2) sY[0][tid] = y0;
         __syncthreads();
-        build_T<L>(sT[buf], sY[buf], tid, nth);
+        build_T_lds<L>(sT[0], sY[0], sTab, tid, nth);
         __syncthreads();
-        const float* T = sT[buf];
 
-        // Work grouped by (l1, l3): for each pair, v_p, dw_p and dx for its
-        // paths, then B_p from the products x[l1 m1] g[l3 m3] formed m1 by m1
-        // and shared by the pair's paths.  A scheduling barrier after each
-        // pair bounds register lifetimes.
-        const rsrc_t dwr = make_row(dw + e * P * C, (long)P * C);
-        float dya[D2];
+        // Per out-edge k: compute with T(k) and the rows already in registers;
+        // then load the rows of edge k+1 into the same registers, reduce dY,
+        // and build T(k+1) in the other buffer while those loads are in flight.
+        for (int k = k0; k < k1; ++k) {
+            const int buf = (k - k0) & 1;
+            const bool has_next = k + 1 < k1;
+            const float* T = sT[buf];
+
+            // Work grouped by (l1, l3): for each pair, v_p, dw_p and dx for its
+            // paths, then B_p from the products x[l1 m1] g[l3 m3] formed m1 by m1
+            // and shared by the pair's paths.  A scheduling barrier after each
+            // pair bounds register lifetimes.
+            const rsrc_t dwr = make_row(dw + e * P * C, (long)P * C);
+            float dya[16];
 #pragma unroll
-        for (int d = 0; d < D2; ++d) dya[d] = 0.0f;
-        static_for<L + 1>([&](auto l1I) __attribute__((always_inline)) {
-            constexpr int l1 = decltype(l1I)::value;
-            static_for<L + 1>([&](auto l3I) __attribute__((always_inline)) {
-                constexpr int l3 = decltype(l3I)::value;
-                constexpr PairPaths pp = pair_paths<S>(l1, l3);
-                if constexpr (pp.n > 0) {
-                    constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
-                    constexpr int o1 = l1 * l1, o3 = l3 * l3;
-                    // (a) v_p = T_p^T g, dw_p = x . v_p, dx += w_p v_p
-                    static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
-                        constexpr int p = pp.p[decltype(kI)::value];
-                        constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
-                        float v[n1][CPL];
-                        static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
-                            constexpr int t = t0 + decltype(tI)::value;
-                            constexpr TSlot s = S::slots[t];
-                            const float tv = T[t];
-#pragma unroll
-                            for (int c = 0; c < CPL; ++c) {
-                                if constexpr (first_m1<S>(t))
-                                    v[s.m1][c] = tv * gv[o3 + s.m3][c];
-                                else
-                                    v[s.m1][c] = __builtin_fmaf(tv, gv[o3 + s.m3][c], v[s.m1][c]);
-                            }
-                        });
-                        float dwv[CPL];
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) {
-                            dwv[c] = xv[o1][c] * v[0][c];
-#pragma unroll
-                            for (int a = 1; a < n1; ++a) dwv[c] = __builtin_fmaf(xv[o1 + a][c], v[a][c], dwv[c]);
-                        }
-                        bstore<CPL>(dwr, voff, (uint32_t)p * opaque_u32((uint32_t)C * 4u), dwv);
-#pragma unroll
-                        for (int a = 0; a < n1; ++a)
-#pragma unroll
-                            for (int c = 0; c < CPL; ++c) {
-                                dxa[o1 + a][c] = __builtin_fmaf(wv[p][c], v[a][c], dxa[o1 + a][c]);
-                                pin_f32(dxa[o1 + a][c]);
-                            }
-                        if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
-                    });
-                    __builtin_amdgcn_sched_barrier(0);
-                    // (b) B_p[m2] = sum C_p[m1][m2][m3] x[m1] g[m3], m1 outermost
-                    float B[kMaxL + 1][2 * kMaxL + 1][CPL];
-                    static_for<n1>([&](auto aI) __attribute__((always_inline)) {
-                        constexpr int a = decltype(aI)::value;
-                        float p3[n3][CPL];
-#pragma unroll
-                        for (int b = 0; b < n3; ++b)
-#pragma unroll
-                            for (int c = 0; c < CPL; ++c) p3[b][c] = xv[o1 + a][c] * gv[o3 + b][c];
+            for (int d = 0; d < 16; ++d) dya[d] = 0.0f;
+            static_for<L + 1>([&](auto l1I) __attribute__((always_inline)) {
+                constexpr int l1 = decltype(l1I)::value;
+                static_for<L + 1>([&](auto l3I) __attribute__((always_inline)) {
+                    constexpr int l3 = decltype(l3I)::value;
+                    constexpr PairPaths pp = pair_paths<S>(l1, l3);
+                    if constexpr (pp.n > 0) {
+                        constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
+                        constexpr int o1 = l1 * l1, o3 = l3 * l3;
+                        // (a) v_p = T_p^T g, dw_p = x . v_p, dx += w_p v_p
                         static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
-                            constexpr int k = decltype(kI)::value;
-                            constexpr int p = pp.p[k];
-                            constexpr int z0 = nz_m1_begin<S>(p, a), z1 = nz_m1_begin<S>(p, a + 1);
-                            static_for<z1 - z0>([&](auto zI) __attribute__((always_inline)) {
-                                constexpr int n = z0 + decltype(zI)::value;
-                                constexpr CgNz nzv = S::nz[n];
+                            constexpr int p = pp.p[decltype(kI)::value];
+                            constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
+                            float v[n1][CPL];
+                            static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
+                                constexpr int t = t0 + decltype(tI)::value;
+                                constexpr TSlot s = S::slots[t];
+                                const float tv = T[t];
 #pragma unroll
                                 for (int c = 0; c < CPL; ++c) {
-                                    if constexpr (nz_first_m2<S>(n))
-                                        B[k][nzv.m2][c] = nzv.c * p3[nzv.m3][c];
+                                    if constexpr (first_m1<S>(t))
+                                        v[s.m1][c] = tv * gv[o3 + s.m3][c];
                                     else
-                                        B[k][nzv.m2][c] = __builtin_fmaf(nzv.c, p3[nzv.m3][c], B[k][nzv.m2][c]);
+                                        v[s.m1][c] = __builtin_fmaf(tv, gv[o3 + s.m3][c], v[s.m1][c]);
                                 }
                             });
+                            float dwv[CPL];
+#pragma unroll
+                            for (int c = 0; c < CPL; ++c) {
+                                dwv[c] = xv[o1][c] * v[0][c];
+#pragma unroll
+                                for (int a = 1; a < n1; ++a) dwv[c] = __builtin_fmaf(xv[o1 + a][c], v[a][c], dwv[c]);
+                            }
+                            bstore<CPL>(dwr, voff, (uint32_t)p * opaque_u32((uint32_t)C * 4u), dwv);
+#pragma unroll
+                            for (int a = 0; a < n1; ++a)
+#pragma unroll
+                                for (int c = 0; c < CPL; ++c) {
+                                    dxa[o1 + a][c] = __builtin_fmaf(wv[p][c], v[a][c], dxa[o1 + a][c]);
+                                    pin_f32(dxa[o1 + a][c]);
+                                }
+                            if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
                         });
-                        if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
-                    });
-                    // (c) dY partial sums
-                    static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
-                        constexpr int k = decltype(kI)::value;
-                        constexpr int p = pp.p[k];
-                        constexpr int n2 = 2 * S::paths[p].l2 + 1, o2 = S::paths[p].l2 * S::paths[p].l2;
+                        __builtin_amdgcn_sched_barrier(0);
+                        // (b) B_p[m2] = sum C_p[m1][m2][m3] x[m1] g[m3], m1 outermost
+                        float B[kMaxL + 1][2 * kMaxL + 1][CPL];
+                        static_for<n1>([&](auto aI) __attribute__((always_inline)) {
+                            constexpr int a = decltype(aI)::value;
+                            float p3[n3][CPL];
 #pragma unroll
-                        for (int b = 0; b < n2; ++b)
+                            for (int b = 0; b < n3; ++b)
 #pragma unroll
-                            for (int c = 0; c < CPL; ++c) dya[o2 + b] = __builtin_fmaf(wv[p][c], B[k][b][c], dya[o2 + b]);
-                    });
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                                for (int c = 0; c < CPL; ++c) p3[b][c] = xv[o1 + a][c] * gv[o3 + b][c];
+                            static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+                                constexpr int kk = decltype(kI)::value;
+                                constexpr int p = pp.p[kk];
+                                constexpr int z0 = nz_m1_begin<S>(p, a), z1 = nz_m1_begin<S>(p, a + 1);
+                                static_for<z1 - z0>([&](auto zI) __attribute__((always_inline)) {
+                                    constexpr int n = z0 + decltype(zI)::value;
+                                    constexpr CgNz nzv = S::nz[n];
+#pragma unroll
+                                    for (int c = 0; c < CPL; ++c) {
+                                        if constexpr (nz_first_m2<S>(n))
+                                            B[kk][nzv.m2][c] = nzv.c * p3[nzv.m3][c];
+                                        else
+                                            B[kk][nzv.m2][c] = __builtin_fmaf(nzv.c, p3[nzv.m3][c], B[kk][nzv.m2][c]);
+                                    }
+                                });
+                            });
+                            if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+                        });
+                        // (c) dY partial sums
+                        static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+                            constexpr int kk = decltype(kI)::value;
+                            constexpr int p = pp.p[kk];
+                            constexpr int n2 = 2 * S::paths[p].l2 + 1, o2 = S::paths[p].l2 * S::paths[p].l2;
+#pragma unroll
+                            for (int b = 0; b < n2; ++b)
+#pragma unroll
+                                for (int c = 0; c < CPL; ++c)
+                                    dya[o2 + b] = __builtin_fmaf(wv[p][c], B[kk][b][c], dya[o2 + b]);
+                        });
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                });
             });
-        });
 
-        // reduce over lanes (DPP, fixed order), then over waves (LDS, fixed order)
-        float tot = 0.0f;
+            // rows of the next edge into the registers just freed (unconditional:
+            // after the last edge the loads use an out-of-range offset and return 0).
+            // The dY sums are pinned first so the loads cannot be hoisted into the
+            // arithmetic above, where their registers would still be in use.
 #pragma unroll
-        for (int d = 0; d < D2; ++d) {
-            const float r = lane_value(wave_sum_to_last(dya[d]), 63);
-            tot = (lane == d) ? r : tot;
-        }
-        if (nwaves > 1) {
-            if (lane < D2) sRed[buf][wave][lane] = tot;
+            for (int d = 0; d < D2; ++d) pin_f32(dya[d]);
+            const long e_cur = e;
+            const int kn = has_next ? k + 1 : k;
+            e = send_perm[kn];
+            // A fresh copy of the thread index each edge keeps the address
+            // arithmetic below from being hoisted out of the loop, where it would
+            // hold registers through the arithmetic above.
+            const int tt = (int)opaque_lane((uint32_t)tid);
+            const int ln = tt & 63;
+            const float ynext = sh_load<D2, VEC>(yv, e, tt);
+            load_bwd_operands<S, CPL>(gv, wv, G, w, send_recv[kn], e, C, has_next ? voff : kOffLane);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // dY: lanes (fixed-order halving), then waves (LDS, fixed order)
+            const float r = wave_sum16(dya, ln);
+            if (sum16_holder(ln)) sRed[tt >> 6][sum16_index(ln)] = r;
+            if (has_next && tt < D2) sY[buf ^ 1][tt] = ynext;
             __syncthreads();
-            if (tid < D2) {
-                float s = sRed[buf][0][tid];
-                for (int q = 1; q < nwaves; ++q) s += sRed[buf][q][tid];
-                tot = s;
+            if (has_next) build_T_lds<L>(sT[buf ^ 1], sY[buf ^ 1], sTab, tt, nth);
+            float tot = 0.0f;
+            if (tt < D2) {
+                tot = sRed[0][tt];
+                for (int q = 1; q < nwaves; ++q) tot += sRed[q][tt];
             }
-        }
-        if constexpr (VEC) {
-            // dvec = (I - r r^T)/|v| * sum_k dY_k grad Y_k(r), lanes < D2 of wave 0
-            if (wave == 0) {
-                const float* vp = yv + 3 * e;
-                const float vx = vp[0], vy = vp[1], vz = vp[2];
-                const float n2 = vx * vx + vy * vy + vz * vz;
-                const float inv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
-                const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
-                float g[3] = {0.0f, 0.0f, 0.0f};
-                if (lane < D2) {
-                    sh_component_grad(lane, rx, ry, rz, g);
-                    g[0] *= tot; g[1] *= tot; g[2] *= tot;
+            if constexpr (VEC) {
+                // dvec = (I - r r^T)/|v| * sum_k dY_k grad Y_k(r), lanes < D2 of wave 0
+                if (tt < 64) {
+                    const float* vp = yv + 3 * e_cur;
+                    const float vx = vp[0], vy = vp[1], vz = vp[2];
+                    const float n2 = vx * vx + vy * vy + vz * vz;
+                    const float inv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+                    const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
+                    float g[3] = {0.0f, 0.0f, 0.0f};
+                    if (ln < D2) {
+                        sh_component_grad(ln, rx, ry, rz, g);
+                        g[0] *= tot; g[1] *= tot; g[2] *= tot;
+                    }
+                    const float gx = lane_value(wave_sum_to_last(g[0]), 63);
+                    const float gy = lane_value(wave_sum_to_last(g[1]), 63);
+                    const float gz = lane_value(wave_sum_to_last(g[2]), 63);
+                    const float rg = rx * gx + ry * gy + rz * gz;
+                    if (ln < 3) {
+                        const float gl = ln == 0 ? gx : (ln == 1 ? gy : gz);
+                        const float rl = ln == 0 ? rx : (ln == 1 ? ry : rz);
+                        dyv[3 * e_cur + ln] = (gl - rg * rl) * inv;
+                    }
                 }
-                const float gx = lane_value(wave_sum_to_last(g[0]), 63);
-                const float gy = lane_value(wave_sum_to_last(g[1]), 63);
-                const float gz = lane_value(wave_sum_to_last(g[2]), 63);
-                const float rg = rx * gx + ry * gy + rz * gz;
-                if (lane < 3) {
-                    const float gl = lane == 0 ? gx : (lane == 1 ? gy : gz);
-                    const float rl = lane == 0 ? rx : (lane == 1 ? ry : rz);
-                    dyv[3 * e + lane] = (gl - rg * rl) * inv;
-                }
+            } else {
+                if (tt < D2) dyv[e_cur * D2 + tt] = tot;
             }
-        } else {
-            if (tid < D2) dyv[e * D2 + tid] = tot;
+            __syncthreads();
         }
     }
 
