@@ -77,6 +77,17 @@ __device__ __forceinline__ void build_T(float* sT, const float* sY, int tid, int
     }
 }
 
+// Entry t of a per-edge T in LDS, read as part of its aligned group of four
+// (T is 16-byte aligned and padded to a multiple of 4 entries): every read is
+// then a 16-byte load at an immediate offset from one address register, and
+// neighbouring entries share it.
+template <int t>
+__device__ __forceinline__ float slot_value(const float* T) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 q = reinterpret_cast<const f4*>(T)[t >> 2];
+    return q[t & 3];
+}
+
 // acc[l3 m3] += sum_p w_p * (T_p^T x[l1])[m3] for one edge and CPL channels.
 template <class S, int CPL>
 __device__ __forceinline__ void edge_forward(float (&acc)[S::D3][CPL], const float (&xv)[S::D1][CPL],
@@ -97,7 +108,7 @@ __device__ __forceinline__ void edge_forward(float (&acc)[S::D3][CPL], const flo
             static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
                 constexpr int t = t0 + decltype(tI)::value;
                 constexpr TSlot s = S::slots[t];
-                const float tv = sT[t];
+                const float tv = slot_value<t>(sT);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
                     acc[o3 + s.m3][c] = __builtin_fmaf(tv, xs[s.m1][c], acc[o3 + s.m3][c]);
@@ -108,7 +119,7 @@ __device__ __forceinline__ void edge_forward(float (&acc)[S::D3][CPL], const flo
             static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
                 constexpr int t = t0 + decltype(tI)::value;
                 constexpr TSlot s = S::slots[t];
-                const float tv = sT[t];
+                const float tv = slot_value<t>(sT);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     if constexpr (first_m3<S>(t))
@@ -135,7 +146,7 @@ __device__ __forceinline__ void load_edge_operands(float (&xv)[S::D1][CPL], floa
 #pragma unroll
     for (int d = 0; d < S::D1; ++d) bload<CPL>(xr, voff, (uint32_t)d * c4, xv[d]);
 #pragma unroll
-    for (int p = 0; p < S::P; ++p) bload<CPL>(wr, voff, (uint32_t)p * c4, wv[p]);
+    for (int p = 0; p < S::P; ++p) bload<CPL, kStream>(wr, voff, (uint32_t)p * c4, wv[p]);
 }
 
 // ------------------------------------------------------------ K1: CSR forward (deterministic)
@@ -171,7 +182,7 @@ __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::D3][CPL], fl
             static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
                 constexpr int t = t0 + decltype(tI)::value;
                 constexpr TSlot s = S::slots[t];
-                const float tv = sT[t];
+                const float tv = slot_value<t>(sT);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
                     acc[o3 + s.m3][c] = __builtin_fmaf(tv, xs[s.m1][c], acc[o3 + s.m3][c]);
@@ -181,7 +192,7 @@ __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::D3][CPL], fl
             static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
                 constexpr int t = t0 + decltype(tI)::value;
                 constexpr TSlot s = S::slots[t];
-                const float tv = sT[t];
+                const float tv = slot_value<t>(sT);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     if constexpr (first_m3<S>(t))
@@ -202,7 +213,7 @@ __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::D3][CPL], fl
             for (int c = 0; c < CPL; ++c) pin_f32(acc[o3 + k][c]);
         // refills for the next edge (loads return 0 when there is none)
         const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
-        bload<CPL>(nw, nvoff, (uint32_t)p * c4, wv[p]);
+        bload<CPL, kStream>(nw, nvoff, (uint32_t)p * c4, wv[p]);
         if constexpr (last_path_of_l1<S>(p)) {
 #pragma unroll
             for (int a = 0; a < n1; ++a) bload<CPL>(nx, nvoff, (uint32_t)(o1 + a) * c4, xv[o1 + a]);
@@ -252,7 +263,7 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
           const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ out) {
     using S = Spec<L, L, L>;
     constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
-    __shared__ float sT[2][NTP];
+    __shared__ __attribute__((aligned(16))) float sT[2][NTP];
     __shared__ float sY[2][16];
     __shared__ SlotDev sTab[NT];
 
@@ -301,7 +312,7 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
     }
     const rsrc_t orow = make_row(out + (long)i * D3 * C, (long)D3 * C);
 #pragma unroll
-    for (int d = 0; d < D3; ++d) bstore<CPL>(orow, voff, (uint32_t)(d * C * 4), acc[d]);
+    for (int d = 0; d < D3; ++d) bstore<CPL, kStream>(orow, voff, (uint32_t)(d * C * 4), acc[d]);
 }
 
 // ------------------------------------------------------------ K2: edge-parallel atomic forward (comparison)
@@ -319,7 +330,7 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
              float* __restrict__ out) {
     using S = Spec<L, L, L>;
     constexpr int D2 = S::D2, D3 = S::D3, NTP = (S::NT + 3) & ~3;
-    __shared__ float sT[NTP];
+    __shared__ __attribute__((aligned(16))) float sT[NTP];
     __shared__ float sY[16];
 
     const long e = blockIdx.x;
@@ -378,7 +389,7 @@ __device__ __forceinline__ void load_bwd_operands(float (&gv)[S::D3][CPL], float
 #pragma unroll
     for (int d = 0; d < S::D3; ++d) bload<CPL>(gr, voff, (uint32_t)d * c4, gv[d]);
 #pragma unroll
-    for (int p = 0; p < S::P; ++p) bload<CPL>(wr, voff, (uint32_t)p * c4, wv[p]);
+    for (int p = 0; p < S::P; ++p) bload<CPL, kStream>(wr, voff, (uint32_t)p * c4, wv[p]);
 }
 
 template <int L, int CPL, bool VEC>
@@ -389,7 +400,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
              float* __restrict__ dyv) {
     using S = Spec<L, L, L>;
     constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
-    __shared__ float sT[2][NTP];
+    __shared__ __attribute__((aligned(16))) float sT[2][NTP];
     __shared__ float sY[2][16];
     __shared__ float sRed[kBwdMaxThreads / 64][16];
     __shared__ SlotDev sTab[NT];
@@ -405,7 +416,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
         const rsrc_t xr = make_row(x + (long)j * D1 * C, (long)D1 * C);
 #pragma unroll
         for (int d = 0; d < D1; ++d) {
-            bload<CPL>(xr, voff, (uint32_t)(d * C * 4), xv[d]);
+            bload<CPL, kStream>(xr, voff, (uint32_t)(d * C * 4), xv[d]);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) dxa[d][c] = 0.0f;
         }
@@ -458,7 +469,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
                             static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
                                 constexpr int t = t0 + decltype(tI)::value;
                                 constexpr TSlot s = S::slots[t];
-                                const float tv = T[t];
+                                const float tv = slot_value<t>(T);
 #pragma unroll
                                 for (int c = 0; c < CPL; ++c) {
                                     if constexpr (first_m1<S>(t))
@@ -474,7 +485,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
 #pragma unroll
                                 for (int a = 1; a < n1; ++a) dwv[c] = __builtin_fmaf(xv[o1 + a][c], v[a][c], dwv[c]);
                             }
-                            bstore<CPL>(dwr, voff, (uint32_t)p * opaque_u32((uint32_t)C * 4u), dwv);
+                            bstore<CPL, kStream>(dwr, voff, (uint32_t)p * opaque_u32((uint32_t)C * 4u), dwv);
 #pragma unroll
                             for (int a = 0; a < n1; ++a)
 #pragma unroll
@@ -589,7 +600,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
 
     const rsrc_t dxr = make_row(dx + (long)j * D1 * C, (long)D1 * C);
 #pragma unroll
-    for (int d = 0; d < D1; ++d) bstore<CPL>(dxr, voff, (uint32_t)(d * C * 4), dxa[d]);
+    for (int d = 0; d < D1; ++d) bstore<CPL, kStream>(dxr, voff, (uint32_t)(d * C * 4), dxa[d]);
 }
 
 // ------------------------------------------------------------ standalone harmonics (vec -> Y, dY -> dvec)

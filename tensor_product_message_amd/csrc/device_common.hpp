@@ -306,18 +306,24 @@ __device__ __forceinline__ void pin_f32(float& v) { asm volatile("" : "+v"(v)); 
 // A lane owns channels c0 + 64 * c (c < CPL): every access instruction then
 // covers 64 consecutive floats (256 contiguous bytes), and channel c's extra
 // 256 bytes go into the scalar offset.
-template <int CPL>
+// Cache policy of a buffer access: kStream (non-temporal) marks the edge
+// streams w and dw, which are touched exactly once, so that they do not evict
+// the gathered node rows that later edges read again.
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
+template <int CPL, int Aux = kCached>
 __device__ __forceinline__ void bload(rsrc_t r, uint32_t voff, uint32_t soff, float (&v)[CPL]) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
-        v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff + 256u * c, 0));
+        v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff + 256u * c, Aux));
 }
 
-template <int CPL>
+template <int CPL, int Aux = kCached>
 __device__ __forceinline__ void bstore(rsrc_t r, uint32_t voff, uint32_t soff, const float (&v)[CPL]) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v[c]), r, voff, soff + 256u * c, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v[c]), r, voff, soff + 256u * c, Aux);
 }
 
 // ------------------------------------------------------------ vector loads
