@@ -653,9 +653,14 @@ struct ChanMap {
     int cpl, waves, tiles;   // channels per lane, waves per workgroup, channel tiles (grid.y)
 };
 
-ChanMap chan_map(int C, int max_waves) {
+// Two channels per lane halve the per-edge overhead (T, loop control) per
+// channel but need twice the registers, so one wave fewer per SIMD; they pay
+// only when the grid has enough rows to fill the chip with fewer waves.
+constexpr long kRowsForTwoChannels = 8192;
+
+ChanMap chan_map(int C, int max_waves, long rows) {
     ChanMap m{};
-    m.cpl = (C % 128 == 0) ? 2 : 1;
+    m.cpl = (C % 128 == 0 && rows >= kRowsForTwoChannels) ? 2 : 1;
     const int per_wave = 64 * m.cpl;
     const int need = (C + per_wave - 1) / per_wave;
     m.waves = need < max_waves ? need : max_waves;
@@ -705,7 +710,7 @@ hipError_t bwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
 
 template <int L>
 hipError_t fwd_L(const LaunchArgs& a, hipStream_t st) {
-    const ChanMap m = chan_map(a.C, kMaxThreads / 64);
+    const ChanMap m = chan_map(a.C, kMaxThreads / 64, a.algo == 0 ? (long)a.n_nodes : a.n_edges);
     return m.cpl == 2 ? fwd_dispatch<L, 2>(a, m, st) : fwd_dispatch<L, 1>(a, m, st);
 }
 

@@ -115,6 +115,16 @@ def test_small_poisson(ctp, dev, n, c, L, y_mode):
     run_small(ctp, dev, d, L, y_mode, 1, bwd=False)
 
 
+@pytest.mark.parametrize("L", [2, 3])
+@pytest.mark.parametrize("y_mode", [0, 1])
+def test_two_channels_per_lane(ctp, dev, L, y_mode):
+    # C = 128 with at least 8192 receivers takes the forward's two-channels-per-lane
+    # mapping (smaller grids use one channel per lane); a sparse graph keeps the
+    # element-by-element oracle comparison fast.
+    d = gen.poisson_small(8192, 128, L, mean_deg=3.0, seed=7 + L)
+    run_small(ctp, dev, d, L, y_mode, 0, bwd=False)
+
+
 def test_deterministic_reruns(ctp, dev):
     d = gen.poisson_small(300, 128, 3, mean_deg=45.0, seed=5)
     g = ctp.Graph(300, T(d["row_ptr"], dev), T(d["senders"], dev))
