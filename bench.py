@@ -221,8 +221,24 @@ def workload_copy(ctp, torch, dev, args):
                 cfg={"workload": "calibration: 1 GiB fp32 device copy"}, cpu=None)
 
 
+def workload_hbm(ctp, torch, dev, args):
+    """Practical HBM ceilings: the library's stream probes (16-byte non-temporal
+    read, write and copy of 2 GiB), the access shape of the kernels' edge streams."""
+    n = (1 << 31) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+
+    def step(t):
+        t.run("read", lambda: ctp.stream_probe(ctp.STREAM_READ, src, dst))
+        t.run("write", lambda: ctp.stream_probe(ctp.STREAM_WRITE, None, dst))
+        t.run("copy", lambda: ctp.stream_probe(ctp.STREAM_COPY, src, dst))
+
+    return dict(step=step, kernel_bytes={"read": 4 * n, "write": 4 * n, "copy": 8 * n}, dominant="copy",
+                edges=0, cfg={"workload": "HBM stream probes: 2 GiB fp32 read, write and copy"}, cpu=None)
+
+
 WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
-             "water": workload_water, "tiny": workload_tiny, "copy": workload_copy}
+             "water": workload_water, "tiny": workload_tiny, "copy": workload_copy, "hbm": workload_hbm}
 
 
 # ------------------------------------------------------------ CPU baseline (oracle)

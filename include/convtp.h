@@ -142,6 +142,17 @@ int32_t conv_tp_build_transpose(int32_t n_nodes, int32_t n_edges, const int32_t 
 int32_t conv_tp_check_graph(int32_t n_nodes, int32_t n_edges, const int32_t *row_ptr, const int32_t *senders,
                             int64_t *n_bad, void *stream);
 
+/* Measurement helper, not part of the operation: plain HBM streams shaped
+ * like the kernels' edge streams (16-byte non-temporal accesses, grid-stride
+ * loop).  kind 0 reads src[n_floats] (dst receives at most one float, only
+ * for a non-finite input), 1 writes dst[n_floats], 2 copies src to dst.  They
+ * measure the bandwidth this device sustains for each traffic mix, against
+ * which the kernels' fractions of the data-sheet HBM peak are read (e3j
+ * abstract: throughput quoted as a fraction of maximum HBM bandwidth).
+ * n_floats must be a multiple of 4; src and dst 16-byte aligned device
+ * pointers.  Enqueued on `stream`. */
+int32_t conv_tp_stream_probe(int32_t kind, const float *src, float *dst, int64_t n_floats, void *stream);
+
 /* Message for the last non-zero status on this thread ("" if none). */
 const char *conv_tp_last_error(void);
 

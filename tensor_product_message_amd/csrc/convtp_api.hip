@@ -247,6 +247,18 @@ int32_t conv_tp_build_transpose(int32_t n_nodes, int32_t n_edges, const int32_t*
                       "conv_tp_build_transpose launch");
 }
 
+int32_t conv_tp_stream_probe(int32_t kind, const float* src, float* dst, int64_t n_floats, void* stream) {
+    if (kind < 0 || kind > 2) return fail(CTP_EINVAL, "kind = %d not 0 (read), 1 (write) or 2 (copy)", kind);
+    if (n_floats < 0 || n_floats % 4 != 0) return fail(CTP_EINVAL, "n_floats = %lld must be a non-negative multiple of 4",
+                                                       (long long)n_floats);
+    if (kind != 1)
+        if (int r = need(src, n_floats, 16, "src")) return r;
+    if (int r = need(dst, kind == 0 ? (n_floats > 0 ? 1 : 0) : n_floats, 16, "dst")) return r;
+    if (n_floats == 0) return ok();
+    return hip_status(ctp::launch_stream_probe(kind, src, dst, (long)n_floats, static_cast<hipStream_t>(stream)),
+                      "stream probe launch");
+}
+
 int32_t conv_tp_check_graph(int32_t n_nodes, int32_t n_edges, const int32_t* row_ptr, const int32_t* senders,
                             int64_t* n_bad, void* stream) {
     if (n_nodes < 0 || n_edges < 0) return fail(CTP_EINVAL, "negative node or edge count");

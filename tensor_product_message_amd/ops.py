@@ -192,6 +192,20 @@ def spherical_harmonics_backward(vec, dY, lmax: int, out=None):
     return out
 
 
+STREAM_READ, STREAM_WRITE, STREAM_COPY = 0, 1, 2
+
+
+def stream_probe(kind: int, src, dst):
+    """HBM stream probe (measurement only): kind STREAM_READ reads src,
+    STREAM_WRITE writes dst, STREAM_COPY copies src into dst."""
+    t = dst if kind == STREAM_WRITE else src
+    n = t.numel()
+    for name, a in (("src", src), ("dst", dst)):
+        if a is not None:
+            _want(a, name, (a.numel(),), device=t.device)
+    check(lib().conv_tp_stream_probe(kind, _p(src), _p(dst), n, _stream(t)))
+
+
 class ConvTPFunction(torch.autograd.Function):
     """Autograd wrapper: forward = conv_tp_fwd (algo 0), backward = conv_tp_bwd."""
 

@@ -138,6 +138,12 @@ def test_other_entry_points_validate(capi):
     assert L.conv_tp_build_transpose(4, 3, A, MIS, A, A, ctypes.c_void_p(0x10001), NUL) == capi.CTP_EALIGN
     assert L.conv_tp_check_graph(4, 3, A, A, None, NUL) == capi.CTP_EINVAL
     assert L.conv_tp_check_graph(4, -3, A, A, None, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(3, A, A2, 16, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(2, A, A2, 18, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(2, NUL, A2, 16, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(1, NUL, NUL, 16, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(0, MIS, A2, 16, NUL) == capi.CTP_EALIGN
+    assert L.conv_tp_stream_probe(2, A, A2, 0, NUL) == capi.CTP_OK
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -357,3 +357,20 @@ def test_water_box_two_layers(ctp, dev):
     # padded edges (zero weight) contribute no weight gradient to the model: w is masked
     assert not host(T(w1, dev))[wb["mask"] == 0].any()
     assert math.isfinite(float(host(h2).sum()))
+
+
+def test_stream_probes(ctp, dev):
+    # measurement helper: the copy is exact, read and write run to completion
+    n = (1 << 20) + 4 * 1000 + 4      # ragged against the grid stride and the 4-deep copy loop
+    src = torch.randn(n, device=dev)
+    dst = torch.zeros(n, device=dev)
+    ctp.stream_probe(ctp.STREAM_COPY, src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    sink = torch.zeros(4, device=dev)
+    ctp.stream_probe(ctp.STREAM_READ, src, sink)
+    ctp.stream_probe(ctp.STREAM_WRITE, None, dst)
+    torch.cuda.synchronize()
+    assert float(sink.abs().sum()) == 0.0
+    assert torch.equal(dst[:8].cpu(), torch.tensor([1.0, 2.0, 3.0, 4.0] * 2))
+    assert bool((dst.view(-1, 4) == torch.tensor([1.0, 2.0, 3.0, 4.0], device=dev)).all())
