@@ -218,7 +218,8 @@ __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::D3][CPL], fl
 #pragma unroll
             for (int a = 0; a < n1; ++a) bload<CPL>(nx, nvoff, (uint32_t)(o1 + a) * c4, xv[o1 + a]);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        // nothing but LDS reads (the next path's T entries) may move across
+        __builtin_amdgcn_sched_barrier(0x100);
     });
 }
 
