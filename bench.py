@@ -30,6 +30,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "conv TP fwd/bwd effective GB/s (% of MI355X HBM peak); edges/s"
 HBM_PEAK_GBS = 8000.0
+# fp32 VALU peak without packed math (the kernels are built with packed fp32
+# switched off): 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
+VALU_PEAK_TFLOPS = 78.6432
 
 
 def fwd_bytes(N, E, C, D1, D2, D3, P, S):
@@ -100,6 +103,26 @@ def shape_of(d, ctp, L, y_mode):
     return N, E, C, D, D, D, P, S
 
 
+def fma_per_edge_channel(ctp, L):
+    """FMAs per (edge, channel) of the plain sparse schedule, from the coupling
+    tables: forward = T entries + min(2l1+1, 2l3+1) per path; backward = T
+    entries (v = T^T g) + 2 * sum(2l1+1) (dw, dx) + x(x)g products per (l1, l3)
+    pair + coupling non-zeros (B) + sum(2l2+1) (dY)."""
+    import numpy as np
+    fwd = bwd = 0
+    pairs = set()
+    for (l1, l2, l3) in ctp.paths(L):
+        c = ctp.coupling(l1, l2, l3)
+        slots = int(np.count_nonzero(np.abs(c).sum(axis=1) > 0))
+        nnz = int(np.count_nonzero(c))
+        n1, n2, n3 = 2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1
+        fwd += slots + min(n1, n3)
+        bwd += slots + 2 * n1 + nnz + n2
+        pairs.add((l1, l3))
+    bwd += sum((2 * a + 1) * (2 * b + 1) for a, b in pairs)
+    return fwd, bwd
+
+
 def workload_l3fb(ctp, torch, dev, args):
     L, y_mode = 3, (ctp.VEC_GIVEN if args.vec else ctp.Y_GIVEN)
     d, g, y = make_poisson(ctp, torch, dev, 16384, 128, L, y_mode, True)
@@ -113,11 +136,13 @@ def workload_l3fb(ctp, torch, dev, args):
         t.run("bwd", lambda: ctp.conv_tp_bwd(G, x, y, w, g, L, y_mode, dx=dx, dw=dw, dy=dy))
 
     kb = {"fwd": fwd_bytes(*shp), "bwd": bwd_bytes(*shp)}
+    ffma, bfma = fma_per_edge_channel(ctp, L)
+    kf = {"fwd": 2.0 * ffma * shp[1] * 128, "bwd": 2.0 * bfma * shp[1] * 128}
     cfg = {"workload": f"lmax=3 conv TP forward+backward, N=16384, C=128, E={shp[1]}, "
                        f"Poisson(45) in-degree, {'vec' if args.vec else 'Y'} given, fp32",
            "n_nodes": shp[0], "n_edges": shp[1], "channels": 128, "lmax": 3,
            "y_mode": "vec" if args.vec else "Y", "paths": shp[6]}
-    return dict(step=step, kernel_bytes=kb, dominant="bwd", edges=shp[1], cfg=cfg,
+    return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=shp[1], cfg=cfg,
                 cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=True))
 
 
@@ -375,6 +400,12 @@ def main():
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "wall_s": round(wall, 3), "kernel_sources_sha": kernel_sources_sha(),
     }
+    if wl.get("kernel_flops"):
+        # the second bound: fp32 VALU arithmetic of the same kernel
+        tf = wl["kernel_flops"][dom] / (dom_ms * 1e-3) / 1e12
+        line["roofline"]["alu"] = {"achieved": round(tf, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": round(tf / VALU_PEAK_TFLOPS, 4),
+                                   "flops": wl["kernel_flops"][dom]}
     if wl.get("cpu") and not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl["cpu"], args.cpu_sample_nodes)
