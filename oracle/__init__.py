@@ -21,6 +21,8 @@ sh      real spherical harmonics (Legendre closed form) and their gradient
 wigner  real Wigner-D matrices from Wigner's small-d formula (tests only)
 convtp  the convolution: numpy materialise-then-scatter definition, and a
         ctypes front to the naive C edge loop in convtp_oracle.c
+nodetp  the node-local channelwise tensor product (same couplings, two node
+        features, per-node weights) and its VJP, numpy
 graph   CSR bookkeeping (row pointers, stable transpose) by numpy sorts
 
 Readings of points the pages leave open (all follow the plainest reading):
