@@ -246,6 +246,27 @@ def workload_copy(ctp, torch, dev, args):
                 cfg={"workload": "calibration: 1 GiB fp32 device copy"}, cpu=None)
 
 
+def workload_node(ctp, torch, dev, args):
+    """Node-local channelwise tensor product, lmax=3, C=128, N=131072 (no graph):
+    forward + backward; every (node, channel) streams its rows once."""
+    from workloads import gen
+    s = gen.NODE
+    L, n, c = s["lmax"], s["n_nodes"], s["channels"]
+    d = gen.node_full(n, c, L, dev, seed=0)
+    x, y, w, G = d["x"], d["y"], d["w"], d["grad_out"]
+    out, dx, dy, dw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)
+    D, P = (L + 1) ** 2, ctp.num_paths(L)
+
+    def step(t):
+        t.run("fwd", lambda: ctp.node_tp_fwd(x, y, w, L, out=out))
+        t.run("bwd", lambda: ctp.node_tp_bwd(G, x, y, w, L, dx=dx, dy=dy, dw=dw))
+
+    kb = {"fwd": 4 * n * c * (3 * D + P), "bwd": 4 * n * c * (5 * D + 2 * P)}
+    cfg = {"workload": f"node-local channelwise tensor product, lmax=3, N={n}, C={c}, forward+backward, fp32",
+           "n_nodes": n, "channels": c, "lmax": L, "paths": P}
+    return dict(step=step, kernel_bytes=kb, dominant="bwd", edges=0, cfg=cfg, cpu=None)
+
+
 def workload_hbm(ctp, torch, dev, args):
     """Practical HBM ceilings: the library's stream probes (16-byte non-temporal
     read, write and copy of 2 GiB), the access shape of the kernels' edge streams."""
@@ -263,7 +284,8 @@ def workload_hbm(ctp, torch, dev, args):
 
 
 WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
-             "water": workload_water, "tiny": workload_tiny, "copy": workload_copy, "hbm": workload_hbm}
+             "water": workload_water, "tiny": workload_tiny, "copy": workload_copy, "hbm": workload_hbm,
+             "node3": workload_node}
 
 
 # ------------------------------------------------------------ CPU baseline (oracle)

@@ -142,6 +142,37 @@ int32_t conv_tp_build_transpose(int32_t n_nodes, int32_t n_edges, const int32_t 
 int32_t conv_tp_check_graph(int32_t n_nodes, int32_t n_edges, const int32_t *row_ptr, const int32_t *senders,
                             int64_t *n_bad, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Node-local channelwise tensor product: the same paths and couplings applied
+ * at each node to two of its own features, with per-node weights (e3j
+ * abstract: tensor-product operations measured against HBM bandwidth;
+ * FlashCart section 4: node-local products beside the edge convolutions):
+ *
+ *   out[i, l3 m3, c] = sum_{p = (l1,l2,l3)} w[i,p,c]
+ *                      sum_{m1,m2} C_p[m1][m2][m3] x[i, l1 m1, c] y[i, l2 m2, c]
+ *
+ * Paths as for the convolution (lexicographic triangle paths, same-l3 paths
+ * summed).  Layout: x[N][D][C], y[N][D][C], w[N][P][C], out[N][D][C], channel
+ * fastest, all device pointers, 16-byte aligned, caller-owned, outputs
+ * overwritten.  l_x = l_y = l_out in 0..3 (CTP_EUNSUPPORTED otherwise), C >= 1.
+ * Every (node, channel) is independent, so results do not depend on the
+ * launch shape and are bitwise reproducible. */
+typedef struct conv_tp_node_problem {
+    int32_t n_nodes;   /* N >= 0 */
+    int32_t channels;  /* C >= 1 */
+    int32_t l_x;       /* max degree of x, 0..3 */
+    int32_t l_y;       /* max degree of y, 0..3 */
+    int32_t l_out;     /* max degree of out, 0..3 */
+} conv_tp_node_problem;
+
+int32_t conv_tp_node_fwd(const conv_tp_node_problem *prob, const float *x, const float *y, const float *w,
+                         float *out, void *stream);
+
+/* Exact VJP for upstream gradient grad_out[N][D][C]: dx, dy (as x, y) and
+ * dw[N][P][C]. */
+int32_t conv_tp_node_bwd(const conv_tp_node_problem *prob, const float *grad_out, const float *x, const float *y,
+                         const float *w, float *dx, float *dy, float *dw, void *stream);
+
 /* Measurement helper, not part of the operation: plain HBM streams shaped
  * like the kernels' edge streams (16-byte non-temporal accesses, grid-stride
  * loop).  kind 0 reads src[n_floats] (dst receives at most one float, only

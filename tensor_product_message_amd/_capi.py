@@ -18,7 +18,8 @@ STATUS_NAMES = {0: "CTP_OK", 1: "CTP_EINVAL", 2: "CTP_EUNSUPPORTED", 3: "CTP_EAL
 # Every symbol include/convtp.h declares.
 EXPORTS = ("conv_tp_num_paths", "conv_tp_paths", "conv_tp_coupling", "conv_tp_fwd", "conv_tp_bwd",
            "conv_tp_sh", "conv_tp_sh_bwd", "conv_tp_build_transpose", "conv_tp_check_graph",
-           "conv_tp_stream_probe", "conv_tp_last_error", "conv_tp_version")
+           "conv_tp_node_fwd", "conv_tp_node_bwd", "conv_tp_stream_probe", "conv_tp_last_error",
+           "conv_tp_version")
 
 
 class Problem(ctypes.Structure):
@@ -26,6 +27,11 @@ class Problem(ctypes.Structure):
                 ("channels", ctypes.c_int32), ("l_in", ctypes.c_int32),
                 ("l_sh", ctypes.c_int32), ("l_out", ctypes.c_int32),
                 ("y_mode", ctypes.c_int32), ("algo", ctypes.c_int32)]
+
+
+class NodeProblem(ctypes.Structure):
+    _fields_ = [("n_nodes", ctypes.c_int32), ("channels", ctypes.c_int32), ("l_x", ctypes.c_int32),
+                ("l_y", ctypes.c_int32), ("l_out", ctypes.c_int32)]
 
 
 class ConvTPError(RuntimeError):
@@ -47,6 +53,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)
     pp = ctypes.POINTER(Problem)
+    npp = ctypes.POINTER(NodeProblem)
     sig = {
         "conv_tp_num_paths": ([i32, i32, i32], i32),
         "conv_tp_paths": ([i32, i32, i32, vp], i32),
@@ -58,6 +65,8 @@ def lib() -> ctypes.CDLL:
         "conv_tp_build_transpose": ([i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "conv_tp_check_graph": ([i32, i32, vp, vp, i64p, vp], i32),
         "conv_tp_stream_probe": ([i32, vp, vp, ctypes.c_int64, vp], i32),
+        "conv_tp_node_fwd": ([npp, vp, vp, vp, vp, vp], i32),
+        "conv_tp_node_bwd": ([npp] + [vp] * 8, i32),
         "conv_tp_last_error": ([], ctypes.c_char_p),
         "conv_tp_version": ([], i32),
     }

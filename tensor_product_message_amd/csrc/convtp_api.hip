@@ -17,6 +17,10 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// node-local products: a row of D * C floats must stay addressable by a
+// 32-bit byte offset
+constexpr int kNodeMaxChannels = 1 << 20;
+
 int fail(int code, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -245,6 +249,56 @@ int32_t conv_tp_build_transpose(int32_t n_nodes, int32_t n_edges, const int32_t*
     return hip_status(ctp::launch_transpose(n_nodes, n_edges, row_ptr, senders, send_ptr, send_perm, send_recv,
                                             static_cast<hipStream_t>(stream)),
                       "conv_tp_build_transpose launch");
+}
+
+namespace {
+
+int check_node_problem(const conv_tp_node_problem* pr) {
+    if (pr == nullptr) return fail(CTP_EINVAL, "problem is null");
+    if (pr->n_nodes < 0) return fail(CTP_EINVAL, "negative node count");
+    if (pr->channels < 1) return fail(CTP_EINVAL, "channels = %d must be >= 1", pr->channels);
+    if (pr->channels > kNodeMaxChannels)
+        return fail(CTP_EUNSUPPORTED, "channels = %d above %d", pr->channels, kNodeMaxChannels);
+    if (int r = check_degree(pr->l_x, "l_x")) return r;
+    if (int r = check_degree(pr->l_y, "l_y")) return r;
+    if (int r = check_degree(pr->l_out, "l_out")) return r;
+    if (pr->l_x != pr->l_y || pr->l_y != pr->l_out)
+        return fail(CTP_EUNSUPPORTED, "degrees (%d,%d,%d) must be equal in this build", pr->l_x, pr->l_y, pr->l_out);
+    return CTP_OK;
+}
+
+}  // namespace
+
+int32_t conv_tp_node_fwd(const conv_tp_node_problem* prob, const float* x, const float* y, const float* w,
+                         float* out, void* stream) {
+    if (int r = check_node_problem(prob)) return r;
+    const int64_t N = prob->n_nodes, C = prob->channels, D = ctp::dim_of(prob->l_x);
+    const int64_t P = ctp::num_paths(prob->l_x, prob->l_y, prob->l_out);
+    if (int r = need(x, N * D * C, 16, "x")) return r;
+    if (int r = need(y, N * D * C, 16, "y")) return r;
+    if (int r = need(w, N * P * C, 16, "w")) return r;
+    if (int r = need(out, N * D * C, 16, "out")) return r;
+    if (N == 0) return ok();
+    return hip_status(ctp::launch_node_fwd(prob->l_x, (int)N, (int)C, x, y, w, out, static_cast<hipStream_t>(stream)),
+                      "node forward launch");
+}
+
+int32_t conv_tp_node_bwd(const conv_tp_node_problem* prob, const float* grad_out, const float* x, const float* y,
+                         const float* w, float* dx, float* dy, float* dw, void* stream) {
+    if (int r = check_node_problem(prob)) return r;
+    const int64_t N = prob->n_nodes, C = prob->channels, D = ctp::dim_of(prob->l_x);
+    const int64_t P = ctp::num_paths(prob->l_x, prob->l_y, prob->l_out);
+    if (int r = need(grad_out, N * D * C, 16, "grad_out")) return r;
+    if (int r = need(x, N * D * C, 16, "x")) return r;
+    if (int r = need(y, N * D * C, 16, "y")) return r;
+    if (int r = need(w, N * P * C, 16, "w")) return r;
+    if (int r = need(dx, N * D * C, 16, "dx")) return r;
+    if (int r = need(dy, N * D * C, 16, "dy")) return r;
+    if (int r = need(dw, N * P * C, 16, "dw")) return r;
+    if (N == 0) return ok();
+    return hip_status(ctp::launch_node_bwd(prob->l_x, (int)N, (int)C, grad_out, x, y, w, dx, dy, dw,
+                                           static_cast<hipStream_t>(stream)),
+                      "node backward launch");
 }
 
 int32_t conv_tp_stream_probe(int32_t kind, const float* src, float* dst, int64_t n_floats, void* stream) {

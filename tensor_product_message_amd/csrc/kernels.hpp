@@ -35,6 +35,10 @@ hipError_t launch_sh_bwd(int L, long n_edges, const float* vec, const float* dY,
 
 hipError_t launch_transpose(int n_nodes, int n_edges, const int32_t* row_ptr, const int32_t* senders,
                             int32_t* send_ptr, int32_t* send_perm, int32_t* send_recv, hipStream_t st);
+hipError_t launch_node_fwd(int L, int n_nodes, int C, const float* x, const float* y, const float* w, float* out,
+                           hipStream_t st);
+hipError_t launch_node_bwd(int L, int n_nodes, int C, const float* G, const float* x, const float* y,
+                           const float* w, float* dx, float* dy, float* dw, hipStream_t st);
 hipError_t launch_stream_probe(int kind, const float* src, float* dst, long n_floats, hipStream_t st);
 hipError_t launch_check_graph(int n_nodes, int n_edges, const int32_t* row_ptr, const int32_t* senders,
                               unsigned long long* d_bad, hipStream_t st);

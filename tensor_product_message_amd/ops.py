@@ -192,6 +192,40 @@ def spherical_harmonics_backward(vec, dY, lmax: int, out=None):
     return out
 
 
+def _node_problem(n, c, lmax):
+    return _capi.NodeProblem(n, c, lmax, lmax, lmax)
+
+
+def node_tp_fwd(x, y, w, lmax: int, out=None):
+    """Node-local channelwise tensor product: out[i] = sum_p w[i,p] (.) C_p(x[i], y[i])."""
+    n, d, c = x.shape
+    _want(x, "x", (n, dim(lmax), c))
+    _want(y, "y", (n, dim(lmax), c), device=x.device)
+    _want(w, "w", (n, num_paths(lmax), c), device=x.device)
+    out = torch.empty_like(x) if out is None else out
+    _want(out, "out", (n, dim(lmax), c), device=x.device)
+    prob = _node_problem(n, c, lmax)
+    check(lib().conv_tp_node_fwd(ctypes.byref(prob), _p(x), _p(y), _p(w), _p(out), _stream(x)))
+    return out
+
+
+def node_tp_bwd(grad_out, x, y, w, lmax: int, dx=None, dy=None, dw=None):
+    """VJP of node_tp_fwd: (dx, dy, dw)."""
+    n, d, c = x.shape
+    for name, t in (("grad_out", grad_out), ("x", x), ("y", y)):
+        _want(t, name, (n, dim(lmax), c), device=x.device)
+    _want(w, "w", (n, num_paths(lmax), c), device=x.device)
+    dx = torch.empty_like(x) if dx is None else dx
+    dy = torch.empty_like(y) if dy is None else dy
+    dw = torch.empty_like(w) if dw is None else dw
+    for name, t, ref in (("dx", dx, x), ("dy", dy, y), ("dw", dw, w)):
+        _want(t, name, tuple(ref.shape), device=x.device)
+    prob = _node_problem(n, c, lmax)
+    check(lib().conv_tp_node_bwd(ctypes.byref(prob), _p(grad_out), _p(x), _p(y), _p(w), _p(dx), _p(dy), _p(dw),
+                                 _stream(x)))
+    return dx, dy, dw
+
+
 STREAM_READ, STREAM_WRITE, STREAM_COPY = 0, 1, 2
 
 

@@ -110,6 +110,31 @@ def test_bwd_rejections(capi):
     assert _bwd(capi, p, g=MIS) == capi.CTP_EALIGN
 
 
+def test_node_entry_points_validate(capi):
+    L = capi.lib()
+    nb = lambda **kw: capi.NodeProblem(**{**dict(n_nodes=4, channels=16, l_x=2, l_y=2, l_out=2), **kw})  # noqa: E731
+    fwd = lambda p, x=A, y=A, w=A, o=A2: L.conv_tp_node_fwd(ctypes.byref(p), x, y, w, o, NUL)  # noqa: E731
+    assert L.conv_tp_node_fwd(None, A, A, A, A2, NUL) == capi.CTP_EINVAL
+    assert fwd(nb(n_nodes=-1)) == capi.CTP_EINVAL
+    assert fwd(nb(channels=0)) == capi.CTP_EINVAL
+    assert fwd(nb(channels=(1 << 20) + 1)) == capi.CTP_EUNSUPPORTED
+    assert fwd(nb(l_x=4, l_y=4, l_out=4)) == capi.CTP_EUNSUPPORTED
+    assert fwd(nb(l_y=1)) == capi.CTP_EUNSUPPORTED
+    for k in ("x", "y", "w", "o"):
+        assert fwd(nb(), **{k: NUL}) == capi.CTP_EINVAL, k
+    assert fwd(nb(), y=MIS) == capi.CTP_EALIGN
+    assert fwd(nb(n_nodes=0), x=NUL, y=NUL, w=NUL, o=NUL) == capi.CTP_OK
+    p = nb()
+    args = [A, A, A, A, A2, A2, A2]
+    for i in range(7):
+        a = list(args)
+        a[i] = NUL
+        assert L.conv_tp_node_bwd(ctypes.byref(p), *a, NUL) == capi.CTP_EINVAL, i
+    a = list(args)
+    a[6] = MIS
+    assert L.conv_tp_node_bwd(ctypes.byref(p), *a, NUL) == capi.CTP_EALIGN
+
+
 def test_empty_arrays_may_be_null(capi):
     # N = 0, E = 0: only row_ptr (one element) is required; the call then
     # succeeds without any kernel, so it is safe without a GPU only if it

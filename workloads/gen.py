@@ -34,6 +34,8 @@ TINY = dict(name="tiny", n_nodes=64, channels=16, lmax=1, deg=16)
 L2_FWD = dict(name="l2fwd", n_nodes=32768, channels=128, lmax=2, mean_deg=45.0)
 L3_FB = dict(name="l3fb", n_nodes=16384, channels=128, lmax=3, mean_deg=45.0)
 SWEEP_CHANNELS = (64, 128, 256, 512, 1024)
+# node-local tensor product (no graph): x, y, G ~ N(0,1) [N][D][C], w [N][P][C]
+NODE = dict(name="node3", n_nodes=131072, channels=128, lmax=3)
 WATER = dict(name="water", n_atoms=1503, box=25.0, cutoff=5.0, n_edges=83325,
              channels=128, lmax=3, n_bessel=8, hidden=64)
 
@@ -243,3 +245,26 @@ def water_box(seed: int = 0, device="cpu", channels: int = 128, lmax: int = 3):
     grad = normal((g["n_nodes"], d, channels), rng)
     g.update(name="water", channels=channels, lmax=lmax, x=x0, w1=w1, w2=w2, grad_out=grad)
     return g
+
+
+def node_small(n_nodes: int, channels: int, lmax: int, seed: int = 0):
+    """Node-local tensor-product inputs drawn on the host: x, y, w, G."""
+    rng = rng_for(seed)
+    d = (lmax + 1) ** 2
+    x = normal((n_nodes, d, channels), rng)
+    y = normal((n_nodes, d, channels), rng)
+    w = normal((n_nodes, num_paths(lmax), channels), rng)
+    g = normal((n_nodes, d, channels), rng)
+    return dict(name=f"node_n{n_nodes}_c{channels}_l{lmax}", n_nodes=n_nodes, channels=channels,
+                lmax=lmax, x=x, y=y, w=w, grad_out=g)
+
+
+def node_full(n_nodes: int, channels: int, lmax: int, device, seed: int = 0):
+    """Full-size node-local inputs drawn on `device` (tags 11 x, 12 y, 13 w, 14 G)."""
+    d = (lmax + 1) ** 2
+    return dict(name=f"node_n{n_nodes}_c{channels}_l{lmax}", n_nodes=n_nodes, channels=channels,
+                lmax=lmax,
+                x=normal_tensor((n_nodes, d, channels), seed, 11, device),
+                y=normal_tensor((n_nodes, d, channels), seed, 12, device),
+                w=normal_tensor((n_nodes, num_paths(lmax), channels), seed, 13, device),
+                grad_out=normal_tensor((n_nodes, d, channels), seed, 14, device))
