@@ -146,6 +146,30 @@ def workload_l3fb(ctp, torch, dev, args):
                 cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=True))
 
 
+def workload_l3dd(ctp, torch, dev, args):
+    """VJP of the VJP at lmax=3, N=16384, C=128, Poisson(45), Y given: the
+    gradients of <ax, dx> + <aw, dw> + <aY, dY> in x, w, Y and G."""
+    from workloads import gen
+    L = 3
+    d, g, y = make_poisson(ctp, torch, dev, 16384, 128, L, ctp.Y_GIVEN, True)
+    ax, aw, aY = gen.cotangents_full(d, dev, seed=0)
+    aY = torch.as_tensor(aY).to(dev)
+    x, w, G = d["x"], d["w"], d["grad_out"]
+    outs = (torch.empty_like(x), torch.empty_like(w), torch.empty_like(y), torch.empty_like(G))
+    n, e, c = 16384, d["n_edges"], 128
+    D, P = (L + 1) ** 2, ctp.num_paths(L)
+
+    def step(t):
+        t.run("dd", lambda: ctp.conv_tp_bwd_bwd(G, x, y, w, ax, aw, aY, g, L, out=outs))
+
+    # each input read once and each output written once: x, ax, G, w, aw, Y, aY,
+    # row_ptr, senders, send_ptr/perm/recv; gx, gG, gw, gY
+    kb = {"dd": 4 * (3 * e * P * c + 3 * e * D + 4 * e + 2 * (n + 1) + 5 * n * D * c)}
+    cfg = {"workload": f"lmax=3 conv TP VJP-of-VJP, N=16384, C=128, E={e}, Poisson(45) in-degree, Y given, fp32",
+           "n_nodes": n, "n_edges": e, "channels": c, "lmax": L, "paths": P}
+    return dict(step=step, kernel_bytes=kb, dominant="dd", edges=e, cfg=cfg, cpu=None)
+
+
 def workload_l2fwd(ctp, torch, dev, args):
     L, y_mode = 2, ctp.Y_GIVEN
     d, g, y = make_poisson(ctp, torch, dev, 32768, 128, L, y_mode, False)
@@ -285,7 +309,7 @@ def workload_hbm(ctp, torch, dev, args):
 
 WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
              "water": workload_water, "tiny": workload_tiny, "copy": workload_copy, "hbm": workload_hbm,
-             "node3": workload_node}
+             "node3": workload_node, "l3dd": workload_l3dd}
 
 
 # ------------------------------------------------------------ CPU baseline (oracle)

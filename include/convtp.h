@@ -120,6 +120,22 @@ int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const fl
                     const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec,
                     void *stream);
 
+/* VJP of the backward (the "VJP-of-VJP" of FlashCart's section on symbolic
+ * VJPs, needed to train on forces), Y given.  With cotangents a_x, a_w, a_y of
+ * conv_tp_bwd's outputs (dx, dw, dY) and L2 = <a_x, dx> + <a_w, dw> + <a_y, dY>,
+ * it writes g_x = dL2/dx [N][D_in][C], g_w = dL2/dw [E][P][C],
+ * g_y = dL2/dY [E][D_sh] and g_grad = dL2/dgrad_out [N][D_out][C]:
+ *   g_grad = F(a_x, w, Y) + F(x, a_w, Y) + F(x, w, a_y)   (F = conv_tp_fwd)
+ *   g_x = dx with (w, Y) -> (a_w, Y) plus (w, a_y); g_w = dw with x -> a_x plus
+ *   Y -> a_y; g_y = dY with x -> a_x plus w -> a_w.
+ * Layouts and graph arrays as for conv_tp_bwd (a_x like x, a_w like w, a_y
+ * like Y).  y_mode must be 0 and algo 0 (CTP_EUNSUPPORTED otherwise); C <= 512.
+ * Every output is written once in a fixed order (bitwise reproducible). */
+int32_t conv_tp_bwd_bwd(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y,
+                        const float *w, const float *a_x, const float *a_w, const float *a_y, const int32_t *row_ptr,
+                        const int32_t *senders, const int32_t *send_ptr, const int32_t *send_perm,
+                        const int32_t *send_recv, float *g_x, float *g_w, float *g_y, float *g_grad, void *stream);
+
 /* Real spherical harmonics of edge vectors: Y[E][(l_sh+1)^2] from vec[E][3]. */
 int32_t conv_tp_sh(int32_t n_edges, int32_t l_sh, const float *vec, float *Y, void *stream);
 

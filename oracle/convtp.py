@@ -206,3 +206,53 @@ def bwd_edges(prob: Problem, x, Y, w, G, row_ptr, senders, rows=None, n_threads=
                           _ptr(G), _ptr(senders), _ptr(recv), rows.size, _ptr(rows),
                           _ptr(dw), _ptr(dY), nt)
     return dw, dY
+
+
+# ------------------------------------------------------------ VJP of the VJP (numpy)
+
+
+def materialised_double_bwd(prob: Problem, x, Y, w, G, ax, aw, aY, row_ptr, senders):
+    """Gradients of  L2 = <ax, dx> + <aw, dw> + <aY, dY>  (the backward's
+    outputs (dx, dw, dY) of materialised_bwd, paired with cotangents ax, aw,
+    aY) with respect to x, w, Y and G: returns (gx, gw, gY, gG).
+
+    The forward is trilinear in (x, w, Y), so each derivative is a sum of the
+    backward's contractions with one operand replaced by its cotangent; the
+    terms are written out per path, message by message (FlashCart, arXiv
+    2610.06409, section on symbolic VJPs: the VJP-of-VJP of the edge
+    convolution)."""
+    x, Y, w, G = (np.asarray(a, dtype=np.float64) for a in (x, Y, w, G))
+    ax, aw, aY = (np.asarray(a, dtype=np.float64) for a in (ax, aw, aY))
+    n, _, c = x.shape
+    recv = _graph.receivers_of(row_ptr)
+    gd = G[recv]
+    gx_e = np.zeros((len(senders), prob.D1, c))
+    gG_e = np.zeros((len(senders), prob.D3, c))
+    gw = np.zeros_like(w)
+    gY = np.zeros_like(Y)
+    for p, (l1, l2, l3) in enumerate(prob.paths):
+        Cp = prob.blocks[p]
+        s1 = slice(l1 * l1, (l1 + 1) ** 2)
+        s2 = slice(l2 * l2, (l2 + 1) ** 2)
+        s3 = slice(l3 * l3, (l3 + 1) ** 2)
+        xs, axs, ys, ays, gs = x[senders, s1, :], ax[senders, s1, :], Y[:, s2], aY[:, s2], gd[:, s3, :]
+        wp, awp = w[:, p, None, :], aw[:, p, None, :]
+        # G enters every term of L2 linearly: gG = the three forwards with one
+        # operand replaced by its cotangent
+        gG_e[:, s3, :] += (wp * np.einsum("abk,eac,eb->ekc", Cp, axs, ys, optimize=True)
+                           + awp * np.einsum("abk,eac,eb->ekc", Cp, xs, ys, optimize=True)
+                           + wp * np.einsum("abk,eac,eb->ekc", Cp, xs, ays, optimize=True))
+        # x appears in <aw, dw> and <aY, dY>
+        gx_e[:, s1, :] += (awp * np.einsum("abk,eb,ekc->eac", Cp, ys, gs, optimize=True)
+                           + wp * np.einsum("abk,eb,ekc->eac", Cp, ays, gs, optimize=True))
+        # w appears in <ax, dx> and <aY, dY>
+        gw[:, p, :] = (np.einsum("abk,eac,eb,ekc->ec", Cp, axs, ys, gs, optimize=True)
+                       + np.einsum("abk,eac,eb,ekc->ec", Cp, xs, ays, gs, optimize=True))
+        # Y appears in <ax, dx> and <aw, dw>
+        gY[:, s2] += (np.einsum("abk,ec,eac,ekc->eb", Cp, w[:, p, :], axs, gs, optimize=True)
+                      + np.einsum("abk,ec,eac,ekc->eb", Cp, aw[:, p, :], xs, gs, optimize=True))
+    gx = np.zeros((n, prob.D1, c))
+    np.add.at(gx, senders, gx_e)
+    gG = np.zeros((n, prob.D3, c))
+    np.add.at(gG, recv, gG_e)
+    return gx, gw, gY, gG

@@ -218,6 +218,56 @@ int32_t conv_tp_bwd(const conv_tp_problem* prob, const float* grad_out, const fl
     return hip_status(ctp::launch_bwd(a, static_cast<hipStream_t>(stream)), "conv_tp_bwd launch");
 }
 
+int32_t conv_tp_bwd_bwd(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* y,
+                        const float* w, const float* a_x, const float* a_w, const float* a_y, const int32_t* row_ptr,
+                        const int32_t* senders, const int32_t* send_ptr, const int32_t* send_perm,
+                        const int32_t* send_recv, float* g_x, float* g_w, float* g_y, float* g_grad, void* stream) {
+    Shape s{};
+    if (int r = check_problem(prob, &s)) return r;
+    if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the double backward has only the deterministic algorithm");
+    if (prob->y_mode != 0) return fail(CTP_EUNSUPPORTED, "the double backward takes Y (y_mode 0)");
+    if (!ctp::dd_supports_channels(prob->channels))
+        return fail(CTP_EUNSUPPORTED, "double backward needs C <= 512, got %d", prob->channels);
+    if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
+    if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
+    if (int r = need(y, s.E * s.D2, 4, "y")) return r;
+    if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;
+    if (int r = need(a_x, s.N * s.D1 * s.C, 16, "a_x")) return r;
+    if (int r = need(a_w, s.E * s.P * s.C, 16, "a_w")) return r;
+    if (int r = need(a_y, s.E * s.D2, 4, "a_y")) return r;
+    if (int r = need(row_ptr, s.N + 1, 4, "row_ptr")) return r;
+    if (int r = need(senders, s.E, 4, "senders")) return r;
+    if (int r = need(send_ptr, s.N + 1, 4, "send_ptr")) return r;
+    if (int r = need(send_perm, s.E, 4, "send_perm")) return r;
+    if (int r = need(send_recv, s.E, 4, "send_recv")) return r;
+    if (int r = need(g_x, s.N * s.D1 * s.C, 16, "g_x")) return r;
+    if (int r = need(g_w, s.E * s.P * s.C, 16, "g_w")) return r;
+    if (int r = need(g_y, s.E * s.D2, 4, "g_y")) return r;
+    if (int r = need(g_grad, s.N * s.D3 * s.C, 16, "g_grad")) return r;
+    ctp::DoubleArgs a{};
+    a.L = prob->l_in;
+    a.n_nodes = prob->n_nodes;
+    a.n_edges = prob->n_edges;
+    a.C = prob->channels;
+    a.x = x;
+    a.ax = a_x;
+    a.y = y;
+    a.ay = a_y;
+    a.w = w;
+    a.aw = a_w;
+    a.grad = grad_out;
+    a.row_ptr = row_ptr;
+    a.senders = senders;
+    a.send_ptr = send_ptr;
+    a.send_perm = send_perm;
+    a.send_recv = send_recv;
+    a.g_x = g_x;
+    a.g_w = g_w;
+    a.g_y = g_y;
+    a.g_grad = g_grad;
+    return hip_status(ctp::launch_double_bwd(a, static_cast<hipStream_t>(stream)), "conv_tp_bwd_bwd launch");
+}
+
 int32_t conv_tp_sh(int32_t n_edges, int32_t l_sh, const float* vec, float* Y, void* stream) {
     if (n_edges < 0) return fail(CTP_EINVAL, "negative edge count");
     if (int r = check_degree(l_sh, "l_sh")) return r;

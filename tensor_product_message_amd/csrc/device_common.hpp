@@ -348,4 +348,52 @@ __device__ __forceinline__ void store_ch(float* __restrict__ p, const float (&v)
     }
 }
 
+// ------------------------------------------------------------ per-edge coupling T in LDS
+
+// Entry t of a per-edge T in LDS, read as part of its aligned group of four
+// (T is 16-byte aligned and padded to a multiple of 4 entries): every read is
+// then a 16-byte load at an immediate offset from one address register, and
+// neighbouring entries share it.
+template <int t>
+__device__ __forceinline__ float slot_value(const float* T) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 q = reinterpret_cast<const f4*>(T)[t >> 2];
+    return q[t & 3];
+}
+
+// Component tid of Y for edge e (lanes >= D2 return 0).
+template <int D2, bool VEC>
+__device__ __forceinline__ float sh_value(const float* __restrict__ yv, long e, int tid) {
+    float r = 0.0f;
+    if (tid < D2) {
+        if constexpr (VEC) {
+            const float* v = yv + 3 * e;
+            r = sh_component(tid, v[0], v[1], v[2]);
+        } else {
+            r = yv[e * D2 + tid];
+        }
+    }
+    return r;
+}
+
+// The same through a buffer row in Y mode: lanes >= D2 read past the row and get 0.
+template <int D2, bool VEC>
+__device__ __forceinline__ float sh_load(const float* __restrict__ yv, long e, int tid) {
+    if constexpr (VEC) {
+        return sh_value<D2, true>(yv, e, tid);
+    } else {
+        const rsrc_t yr = make_row(yv + e * D2, D2);
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(yr, (uint32_t)tid * 4u, 0, 0));
+    }
+}
+
+template <int L>
+__device__ __forceinline__ void build_T_lds(float* sT, const float* sY, const SlotDev* tab, int tid, int nth) {
+    constexpr int NT = Spec<L, L, L>::NT;
+    for (int t = tid; t < NT; t += nth) {
+        const SlotDev s = tab[t];
+        sT[t] = s.c1 * sY[s.yy & 0xff] + s.c2 * sY[s.yy >> 8];
+    }
+}
+
 }  // namespace ctp

@@ -27,7 +27,24 @@ struct LaunchArgs {
     float* dy;             // dY[E][D] or dvec[E][3]
 };
 
+// VJP of the VJP (Y given): cotangents ax, aw, ay of (dx, dw, dY).
+struct DoubleArgs {
+    int L;
+    int n_nodes, n_edges, C;
+    const float *x, *ax;    // [N][D][C]
+    const float *y, *ay;    // [E][D]
+    const float *w, *aw;    // [E][P][C]
+    const float* grad;      // G [N][D][C]
+    const int32_t *row_ptr, *senders, *send_ptr, *send_perm, *send_recv;
+    float* g_x;             // [N][D][C]
+    float* g_w;             // [E][P][C]
+    float* g_y;             // [E][D]
+    float* g_grad;          // [N][D][C]
+};
+
 hipError_t launch_fwd(const LaunchArgs& a, hipStream_t st);
+hipError_t launch_double_bwd(const DoubleArgs& a, hipStream_t st);
+bool dd_supports_channels(int C);
 hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st);
 bool bwd_supports_channels(int C);
 hipError_t launch_sh(int L, long n_edges, const float* vec, float* Y, hipStream_t st);

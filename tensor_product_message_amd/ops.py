@@ -173,6 +173,27 @@ def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int =
     return dx, dw, dy
 
 
+def conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph: Graph, lmax: int, out=None):
+    """VJP of conv_tp_bwd (Y given): gradients (g_x, g_w, g_y, g_grad) of
+    <a_x, dx> + <a_w, dw> + <a_y, dY> (see include/convtp.h)."""
+    n, e, c = _shapes(x, Y, w, graph, lmax, Y_GIVEN)
+    _want(grad_out, "grad_out", (n, dim(lmax), c), device=x.device)
+    _want(a_x, "a_x", x.shape, device=x.device)
+    _want(a_w, "a_w", w.shape, device=x.device)
+    _want(a_y, "a_y", Y.shape, device=x.device)
+    send_ptr, send_perm, send_recv = graph.transpose
+    if out is None:
+        out = (torch.empty_like(x), torch.empty_like(w), torch.empty_like(Y), torch.empty_like(grad_out))
+    g_x, g_w, g_y, g_grad = out
+    for name, t, ref in (("g_x", g_x, x), ("g_w", g_w, w), ("g_y", g_y, Y), ("g_grad", g_grad, grad_out)):
+        _want(t, name, ref.shape, device=x.device)
+    prob = _problem(n, e, c, lmax, Y_GIVEN, ALGO_CSR)
+    check(lib().conv_tp_bwd_bwd(ctypes.byref(prob), _p(grad_out), _p(x), _p(Y), _p(w), _p(a_x), _p(a_w),
+                                _p(a_y), _p(graph.row_ptr), _p(graph.senders), _p(send_ptr), _p(send_perm),
+                                _p(send_recv), _p(g_x), _p(g_w), _p(g_y), _p(g_grad), _stream(x)))
+    return g_x, g_w, g_y, g_grad
+
+
 def spherical_harmonics(vec, lmax: int, out=None):
     e = vec.shape[0]
     _want(vec, "vec", (e, 3))

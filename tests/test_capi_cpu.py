@@ -135,6 +135,28 @@ def test_node_entry_points_validate(capi):
     assert L.conv_tp_node_bwd(ctypes.byref(p), *a, NUL) == capi.CTP_EALIGN
 
 
+def _bwd_bwd(capi, prob, args):
+    return capi.lib().conv_tp_bwd_bwd(ctypes.byref(prob), *args, NUL)
+
+
+def test_bwd_bwd_rejections(capi):
+    args = [A] * 12 + [A2] * 4      # 12 inputs (grad_out .. send_recv), 4 outputs
+    assert _bwd_bwd(capi, _prob(capi, y_mode=1), args) == capi.CTP_EUNSUPPORTED
+    assert _bwd_bwd(capi, _prob(capi, algo=1), args) == capi.CTP_EUNSUPPORTED
+    assert _bwd_bwd(capi, _prob(capi, channels=513), args) == capi.CTP_EUNSUPPORTED
+    assert len(args) == len(capi.lib().conv_tp_bwd_bwd.argtypes) - 2
+    for k in range(16):
+        a = list(args)
+        a[k] = NUL
+        assert _bwd_bwd(capi, _prob(capi), a) == capi.CTP_EINVAL, k
+    a = list(args)
+    a[5] = MIS          # a_w
+    assert _bwd_bwd(capi, _prob(capi), a) == capi.CTP_EALIGN
+    a = [NUL] * 16
+    a[7] = a[9] = A     # empty graph: only row_ptr and send_ptr (N+1 = 1 entry); nothing is launched
+    assert _bwd_bwd(capi, _prob(capi, n_nodes=0, n_edges=0), a) == capi.CTP_OK
+
+
 def test_empty_arrays_may_be_null(capi):
     # N = 0, E = 0: only row_ptr (one element) is required; the call then
     # succeeds without any kernel, so it is safe without a GPU only if it

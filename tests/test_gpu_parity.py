@@ -374,3 +374,65 @@ def test_stream_probes(ctp, dev):
     assert float(sink.abs().sum()) == 0.0
     assert torch.equal(dst[:8].cpu(), torch.tensor([1.0, 2.0, 3.0, 4.0] * 2))
     assert bool((dst.view(-1, 4) == torch.tensor([1.0, 2.0, 3.0, 4.0], device=dev)).all())
+
+
+# ------------------------------------------------------------ VJP of the VJP (Y given)
+
+
+def run_double_small(ctp, dev, d, L):
+    n = d["n_nodes"]
+    prob = oc.Problem(L, L, L)
+    Y = sh32(L, d["vec"])
+    ax, aw, aY = gen.cotangents_small(d, seed=n)
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    res = ctp.conv_tp_bwd_bwd(T(d["grad_out"], dev), T(d["x"], dev), T(Y, dev), T(d["w"], dev),
+                              T(ax, dev), T(aw, dev), T(aY, dev), g, L)
+    ref = oc.materialised_double_bwd(prob, d["x"], Y, d["w"], d["grad_out"], ax, aw, aY,
+                                     d["row_ptr"], d["senders"])
+    for name, got, want in zip(("g_x", "g_w", "g_y", "g_grad"), res, ref):
+        close(name, host(got), want)
+    return res
+
+
+def test_double_bwd_tiny(ctp, dev):
+    run_double_small(ctp, dev, gen.tiny(), 1)
+
+
+@pytest.mark.parametrize("n,c,L", [(90, 16, 1), (150, 48, 2), (120, 128, 2), (100, 128, 3), (70, 64, 3),
+                                   (60, 192, 3), (40, 96, 0), (36, 512, 2)])
+def test_double_bwd_small(ctp, dev, n, c, L):
+    d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=n + c + L)
+    a = run_double_small(ctp, dev, d, L)
+    b = run_double_small(ctp, dev, d, L)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_double_bwd_full_l3_sampled(ctp, dev):
+    """lmax=3, N=16384, C=128, Poisson(45): every output on seeded samples,
+    the oracle composed from the C edge loop with swapped operands."""
+    n, c, L = 16384, 128, 3
+    d = gen.poisson_full(n, c, L, dev, seed=0)
+    rp, s = d["row_ptr"], d["senders"]
+    prob = oc.Problem(L, L, L)
+    Y = sh32(L, d["vec"])
+    ax, aw, aY = gen.cotangents_full(d, dev, seed=0)
+    g = ctp.Graph(n, T(rp, dev), T(s, dev))
+    gx, gw, gy, gG = ctp.conv_tp_bwd_bwd(d["grad_out"], d["x"], T(Y, dev), d["w"], ax, aw, T(aY, dev), g, L)
+    Yr, aYr = Y.astype(np.float64), aY.astype(np.float64)
+    x_h, ax_h, G_h = host(d["x"]), host(ax), host(d["grad_out"])
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(n, 24, replace=False))
+    ri = torch.as_tensor(rows, device=dev)
+    ref_G = (_sub_fwd(prob, rp, s, Yr, d["w"], ax_h, rows) + _sub_fwd(prob, rp, s, Yr, aw, x_h, rows)
+             + _sub_fwd(prob, rp, s, aYr, d["w"], x_h, rows))
+    close("g_grad[sample]", host(gG[ri]), ref_G)
+    ref_x = _sub_dx(prob, rp, s, Yr, aw, G_h, rows) + _sub_dx(prob, rp, s, aYr, d["w"], G_h, rows)
+    close("g_x[sample]", host(gx[ri]), ref_x)
+    edges = np.sort(rng.choice(len(s), 96, replace=False))
+    dw1, dY1 = _sub_edges(prob, rp, s, Yr, d["w"], ax_h, G_h, edges)
+    dw2, _ = _sub_edges(prob, rp, s, aYr, d["w"], x_h, G_h, edges)
+    _, dY3 = _sub_edges(prob, rp, s, Yr, aw, x_h, G_h, edges)
+    ei = torch.as_tensor(edges, device=dev)
+    close("g_w[sample]", host(gw[ei]), dw1 + dw2)
+    close("g_y[sample]", host(gy[ei]), dY1 + dY3)

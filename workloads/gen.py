@@ -268,3 +268,20 @@ def node_full(n_nodes: int, channels: int, lmax: int, device, seed: int = 0):
                 y=normal_tensor((n_nodes, d, channels), seed, 12, device),
                 w=normal_tensor((n_nodes, num_paths(lmax), channels), seed, 13, device),
                 grad_out=normal_tensor((n_nodes, d, channels), seed, 14, device))
+
+
+def cotangents_small(d: dict, seed: int = 0):
+    """Cotangents (ax, aw, aY) of the backward's outputs for a small workload,
+    N(0,1) fp32 from their own PCG64 stream."""
+    rng = rng_for(seed + 7919)
+    return (normal(d["x"].shape, rng), normal(d["w"].shape, rng),
+            normal((d["n_edges"], (d["lmax"] + 1) ** 2), rng))
+
+
+def cotangents_full(d: dict, device, seed: int = 0):
+    """Full-size cotangents: ax and aw on `device` (tags 4, 5), aY on the host."""
+    n, e, c, L = d["n_nodes"], d["n_edges"], d["x"].shape[2], d["lmax"]
+    ax = normal_tensor(d["x"].shape, seed, 4, device)
+    aw = normal_tensor((e, num_paths(L), c), seed, 5, device)
+    aY = normal((e, (L + 1) ** 2), rng_for(seed + 7919))
+    return ax, aw, aY
