@@ -43,14 +43,16 @@ def bwd_bytes(N, E, C, D1, D2, D3, P, S):
     return 4 * (2 * E * P * C + 2 * E * S + 2 * E + (N + 1) + 2 * N * C * D1 + N * C * D3)
 
 
-KERNEL_SOURCES = ("convtp_kernels.hip", "device_common.hpp", "tables.hpp", "kernels.hpp")
+KERNEL_HEADERS = ("device_common.hpp", "tables.hpp", "kernels.hpp")
+# the source each workload's kernels are compiled from (besides the headers)
+WORKLOAD_SOURCE = {"node3": "nodetp_kernels.hip", "l3dd": "convtp_dd_kernels.hip", "hbm": "stream_probe.hip"}
 
 
-def kernel_sources_sha():
-    """Hash of the sources the conv TP kernels are compiled from."""
+def kernel_sources_sha(workload="l3fb"):
+    """Hash of the sources the workload's kernels are compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_product_message_amd", "csrc")
-    for f in KERNEL_SOURCES:
+    for f in (WORKLOAD_SOURCE.get(workload, "convtp_kernels.hip"),) + KERNEL_HEADERS:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -165,9 +167,10 @@ def workload_l3dd(ctp, torch, dev, args):
     # each input read once and each output written once: x, ax, G, w, aw, Y, aY,
     # row_ptr, senders, send_ptr/perm/recv; gx, gG, gw, gY
     kb = {"dd": 4 * (3 * e * P * c + 3 * e * D + 4 * e + 2 * (n + 1) + 5 * n * D * c)}
+    kf = {"dd": 2.0 * dd_fma_per_edge_channel(ctp, L) * e * c}
     cfg = {"workload": f"lmax=3 conv TP VJP-of-VJP, N=16384, C=128, E={e}, Poisson(45) in-degree, Y given, fp32",
            "n_nodes": n, "n_edges": e, "channels": c, "lmax": L, "paths": P}
-    return dict(step=step, kernel_bytes=kb, dominant="dd", edges=e, cfg=cfg, cpu=None)
+    return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="dd", edges=e, cfg=cfg, cpu=None)
 
 
 def workload_l2fwd(ctp, torch, dev, args):
@@ -270,6 +273,38 @@ def workload_copy(ctp, torch, dev, args):
                 cfg={"workload": "calibration: 1 GiB fp32 device copy"}, cpu=None)
 
 
+def node_fma_per_node_channel(ctp, L):
+    """FMAs per (node, channel) of the node-local product: forward = x*y
+    products per (l1, l2) pair + coupling non-zeros + sum(2l3+1) (w scaling);
+    backward = that for dw (plus sum(2l3+1) for the dot with g), and the same
+    count for dx (y*g products per (l2, l3)) and dy (x*g per (l1, l3))."""
+    import numpy as np
+    ps = ctp.paths(L)
+    nnz = sum(int(np.count_nonzero(ctp.coupling(*p))) for p in ps)
+    def prod(i, j):
+        return sum((2 * a + 1) * (2 * b + 1) for a, b in {(p[i], p[j]) for p in ps})
+    s1 = sum(2 * p[0] + 1 for p in ps)
+    s2 = sum(2 * p[1] + 1 for p in ps)
+    s3 = sum(2 * p[2] + 1 for p in ps)
+    fwd = prod(0, 1) + nnz + s3
+    bwd = (prod(0, 1) + nnz + s3) + (prod(1, 2) + nnz + s1) + (prod(0, 2) + nnz + s2)
+    return fwd, bwd
+
+
+def dd_fma_per_edge_channel(ctp, L):
+    """FMAs per (edge, channel) of the VJP of the VJP: receiver kernel
+    3 sum(2l1+1) + 2 T entries; sender kernel 2 T entries + 4 sum(2l1+1) +
+    2 (x*g products per (l1, l3) + coupling non-zeros + sum(2l2+1))."""
+    import numpy as np
+    ps = ctp.paths(L)
+    slots = sum(int(np.count_nonzero(np.abs(ctp.coupling(*p)).sum(axis=1) > 0)) for p in ps)
+    nnz = sum(int(np.count_nonzero(ctp.coupling(*p))) for p in ps)
+    s1 = sum(2 * p[0] + 1 for p in ps)
+    s2 = sum(2 * p[1] + 1 for p in ps)
+    pairs = sum((2 * a + 1) * (2 * b + 1) for a, b in {(p[0], p[2]) for p in ps})
+    return 3 * s1 + 2 * slots + 2 * slots + 4 * s1 + 2 * (pairs + nnz + s2)
+
+
 def workload_node(ctp, torch, dev, args):
     """Node-local channelwise tensor product, lmax=3, C=128, N=131072 (no graph):
     forward + backward; every (node, channel) streams its rows once."""
@@ -286,9 +321,11 @@ def workload_node(ctp, torch, dev, args):
         t.run("bwd", lambda: ctp.node_tp_bwd(G, x, y, w, L, dx=dx, dy=dy, dw=dw))
 
     kb = {"fwd": 4 * n * c * (3 * D + P), "bwd": 4 * n * c * (5 * D + 2 * P)}
+    ff, bf = node_fma_per_node_channel(ctp, L)
+    kf = {"fwd": 2.0 * ff * n * c, "bwd": 2.0 * bf * n * c}
     cfg = {"workload": f"node-local channelwise tensor product, lmax=3, N={n}, C={c}, forward+backward, fp32",
            "n_nodes": n, "channels": c, "lmax": L, "paths": P}
-    return dict(step=step, kernel_bytes=kb, dominant="bwd", edges=0, cfg=cfg, cpu=None)
+    return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=0, cfg=cfg, cpu=None)
 
 
 def workload_hbm(ctp, torch, dev, args):
@@ -368,13 +405,13 @@ def cpu_baseline(spec, sample_nodes):
 # ------------------------------------------------------------ traffic from committed counters
 
 
-def committed_traffic(kernel_tag):
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.json")
+def committed_traffic(workload, kernel):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{kernel}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha") != kernel_sources_sha():
+    if rec.get("source_sha") != kernel_sources_sha(workload):
         return None        # kernels changed since the counters were taken
     return rec.get("bytes_per_launch")
 
@@ -433,7 +470,7 @@ def main():
                    "pct_hbm_peak": round(100 * wl["kernel_bytes"][k] / (timer.mean_ms(k) * 1e-3) / 1e9
                                          / HBM_PEAK_GBS, 1)}
                for k in wl["kernel_bytes"]}
-    traffic = committed_traffic(f"{args.workload}_{dom}")
+    traffic = committed_traffic(args.workload, dom)
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_value, 4),
@@ -444,7 +481,7 @@ def main():
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "wall_s": round(wall, 3), "kernel_sources_sha": kernel_sources_sha(),
+        "wall_s": round(wall, 3), "kernel_sources_sha": kernel_sources_sha(args.workload),
     }
     if wl.get("kernel_flops"):
         # the second bound: fp32 VALU arithmetic of the same kernel
