@@ -97,15 +97,15 @@ def make_poisson(ctp, torch, dev, n, c, L, y_mode, with_bwd, seed=0):
     return d, g, y
 
 
-def shape_of(d, ctp, L, y_mode):
+def shape_of(d, ctp, L, y_mode, variant=0):
     N, E, C = d["n_nodes"], d["n_edges"], d["channels"]
     D = ctp.dim(L)
-    P = ctp.num_paths(L)
+    paths, DO = ctp.layout(L, variant)
     S = D if y_mode == ctp.Y_GIVEN else 3
-    return N, E, C, D, D, D, P, S
+    return N, E, C, D, D, DO, len(paths), S
 
 
-def fma_per_edge_channel(ctp, L):
+def fma_per_edge_channel(ctp, L, variant=0):
     """FMAs per (edge, channel) of the plain sparse schedule, from the coupling
     tables: forward = T entries + min(2l1+1, 2l3+1) per path; backward = T
     entries (v = T^T g) + 2 * sum(2l1+1) (dw, dx) + x(x)g products per (l1, l3)
@@ -113,15 +113,16 @@ def fma_per_edge_channel(ctp, L):
     import numpy as np
     fwd = bwd = 0
     pairs = set()
-    for (l1, l2, l3) in ctp.paths(L):
+    for k, (l1, l2, l3) in enumerate(ctp.layout(L, variant)[0]):
         c = ctp.coupling(l1, l2, l3)
         slots = int(np.count_nonzero(np.abs(c).sum(axis=1) > 0))
         nnz = int(np.count_nonzero(c))
         n1, n2, n3 = 2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1
         fwd += slots + min(n1, n3)
         bwd += slots + 2 * n1 + nnz + n2
-        pairs.add((l1, l3))
-    bwd += sum((2 * a + 1) * (2 * b + 1) for a, b in pairs)
+        # products x (x) g are shared by the paths reading the same G block
+        pairs.add((l1, l3) if variant == 0 else (l1, l3, k))
+    bwd += sum((2 * q[0] + 1) * (2 * q[1] + 1) for q in pairs)
     return fwd, bwd
 
 
@@ -171,6 +172,33 @@ def workload_l3dd(ctp, torch, dev, args):
     cfg = {"workload": f"lmax=3 conv TP VJP-of-VJP, N=16384, C=128, E={e}, Poisson(45) in-degree, Y given, fp32",
            "n_nodes": n, "n_edges": e, "channels": c, "lmax": L, "paths": P}
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="dd", edges=e, cfg=cfg, cpu=None)
+
+
+def workload_l3mace(ctp, torch, dev, args):
+    """MACE variant at lmax=3, N=16384, C=128, Poisson(45), Y given: natural-parity
+    paths (P=23), one output slot per path (99 components per channel)."""
+    from workloads import gen
+    L, V = 3, ctp.SLOTS
+    d, g, y = make_poisson(ctp, torch, dev, 16384, 128, L, ctp.Y_GIVEN, False)
+    shp = shape_of(d, ctp, L, ctp.Y_GIVEN, V)
+    n, e, c = shp[0], shp[1], shp[2]
+    x = d["x"]
+    w = gen.normal_tensor((e, shp[6], c), 0, 21, dev)
+    G = gen.normal_tensor((n, shp[5], c), 0, 23, dev)
+    g.transpose
+    out, dx, dw, dy = torch.empty_like(G), torch.empty_like(x), torch.empty_like(w), torch.empty_like(y)
+
+    def step(t):
+        t.run("fwd", lambda: ctp.conv_tp_fwd(x, y, w, g, L, ctp.Y_GIVEN, out=out, variant=V))
+        t.run("bwd", lambda: ctp.conv_tp_bwd(G, x, y, w, g, L, ctp.Y_GIVEN, dx=dx, dw=dw, dy=dy, variant=V))
+
+    kb = {"fwd": fwd_bytes(*shp), "bwd": bwd_bytes(*shp)}
+    ffma, bfma = fma_per_edge_channel(ctp, L, V)
+    kf = {"fwd": 2.0 * ffma * e * c, "bwd": 2.0 * bfma * e * c}
+    cfg = {"workload": f"MACE variant (natural-parity paths, per-path output slots), lmax=3, N=16384, C=128, "
+                       f"E={e}, Poisson(45) in-degree, Y given, fp32",
+           "n_nodes": n, "n_edges": e, "channels": c, "lmax": L, "paths": shp[6], "out_dim": shp[5]}
+    return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=e, cfg=cfg, cpu=None)
 
 
 def workload_l2fwd(ctp, torch, dev, args):
@@ -346,7 +374,7 @@ def workload_hbm(ctp, torch, dev, args):
 
 WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
              "water": workload_water, "tiny": workload_tiny, "copy": workload_copy, "hbm": workload_hbm,
-             "node3": workload_node, "l3dd": workload_l3dd}
+             "node3": workload_node, "l3dd": workload_l3dd, "l3mace": workload_l3mace}
 
 
 # ------------------------------------------------------------ CPU baseline (oracle)

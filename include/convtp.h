@@ -30,6 +30,7 @@
  *
  * Layout (all arrays contiguous, channel index fastest):
  *   x[N][D_in][C], out[N][D_out][C], grad_out[N][D_out][C], dx[N][D_in][C]
+ *   (D_out = (l_out+1)^2 for variant 0; for variant 1 see conv_tp_problem)
  *   w[E][P][C], dw[E][P][C]
  *   Y[E][D_sh] (y_mode 0) or vec[E][3] (y_mode 1); dY / dvec alike
  *   row_ptr[N+1], senders[E]: CSR by receiver (edges of receiver i are
@@ -87,15 +88,28 @@ typedef struct conv_tp_problem {
     int32_t l_out;     /* max degree of out, 0..3 (this build: l_in = l_sh = l_out) */
     int32_t y_mode;    /* 0: Y[E][D_sh] given; 1: vec[E][3] given, Y evaluated in-kernel */
     int32_t algo;      /* 0: CSR segmented sum, deterministic; 1: edge-parallel atomics (forward only) */
+    int32_t variant;   /* 0: every triangle path, same-l3 paths summed into one block of D_out = (l_out+1)^2;
+                          1: MACE's convolution - natural-parity paths only (l1+l2+l3 even; e3j Table 3's
+                          MACE model, FlashCart's admissible-coupling section), each path with an output
+                          slot of its own: out[N][D_out][C] with D_out = sum over paths of 2 l3 + 1, slots
+                          in path order.  grad_out has the same layout as out.  See conv_tp_layout. */
 } conv_tp_problem;
 
-/* Number of paths P for the degrees, or -1 (with a message) if a degree is
- * outside 0..3.  Pure host function. */
+/* Number of paths P of variant 0 for the degrees, or -1 (with a message) if a
+ * degree is outside 0..3.  Pure host function. */
 int32_t conv_tp_num_paths(int32_t l_in, int32_t l_sh, int32_t l_out);
 
-/* Path list: l123 (host, [P][3]) receives (l1, l2, l3) of every path in the
- * order of w's second index.  Pure host function. */
+/* Path list of variant 0: l123 (host, [P][3]) receives (l1, l2, l3) of every
+ * path in the order of w's second index.  Pure host function. */
 int32_t conv_tp_paths(int32_t l_in, int32_t l_sh, int32_t l_out, int32_t *l123);
+
+/* Path list and output width of a variant: *n_paths = P, *out_dim = D_out
+ * (components per channel of out and grad_out), and, if l123 (host,
+ * [P][3]) is not null, the paths in the order of w's second index.  Pure host
+ * function; CTP_EINVAL for an unknown variant or a null count pointer,
+ * CTP_EUNSUPPORTED for a degree outside 0..3. */
+int32_t conv_tp_layout(int32_t variant, int32_t l_in, int32_t l_sh, int32_t l_out, int32_t *n_paths,
+                       int32_t *out_dim, int32_t *l123);
 
 /* The library's real coupling tensor of path (l1, l2, l3) in double
  * precision: out (host, [2l1+1][2l2+1][2l3+1]).  The kernels use these
@@ -203,7 +217,7 @@ int32_t conv_tp_stream_probe(int32_t kind, const float *src, float *dst, int64_t
 /* Message for the last non-zero status on this thread ("" if none). */
 const char *conv_tp_last_error(void);
 
-/* ABI version (major * 100 + minor). */
+/* ABI version (major * 100 + minor): 101 added conv_tp_problem.variant. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

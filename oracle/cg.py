@@ -25,13 +25,15 @@ from functools import lru_cache
 import numpy as np
 
 
-def paths(l_in: int, l_sh: int, l_out: int):
-    """All triangle-allowed (l1, l2, l3), lexicographic."""
+def paths(l_in: int, l_sh: int, l_out: int, natural: bool = False):
+    """All triangle-allowed (l1, l2, l3), lexicographic; with natural=True only
+    the natural-parity ones (l1 + l2 + l3 even: FlashCart, arXiv 2610.06409,
+    background section, restricts its products to these)."""
     return [(l1, l2, l3)
             for l1 in range(l_in + 1)
             for l2 in range(l_sh + 1)
             for l3 in range(l_out + 1)
-            if abs(l1 - l2) <= l3 <= l1 + l2]
+            if abs(l1 - l2) <= l3 <= l1 + l2 and (not natural or (l1 + l2 + l3) % 2 == 0)]
 
 
 def _f(n: int) -> int:

@@ -52,9 +52,9 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int
-        L.oracle_fwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P, I]
-        L.oracle_bwd_dx.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, I]
-        L.oracle_bwd_edge.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, I]
+        L.oracle_fwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, I]
+        L.oracle_bwd_dx.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
+        L.oracle_bwd_edge.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, P, I]
         for f in (L.oracle_fwd, L.oracle_bwd_dx, L.oracle_bwd_edge):
             f.restype = I
         L.oracle_max_threads.restype = I
@@ -67,13 +67,27 @@ def max_threads() -> int:
 
 
 class Problem:
-    """Path list and dense coupling blocks for (l_in, l_sh, l_out)."""
+    """Path list, output blocks and dense coupling blocks for (l_in, l_sh, l_out).
 
-    def __init__(self, l_in: int, l_sh: int, l_out: int):
-        self.l_in, self.l_sh, self.l_out = l_in, l_sh, l_out
-        self.paths = _cg.paths(l_in, l_sh, l_out)
+    variant 0: every triangle path; paths sharing l3 add into one output block
+    (l3^2 .. (l3+1)^2 - 1).  variant 1 (MACE's convolution, the implementation
+    e3j's Table 2 matches): natural-parity paths only, each writing an output
+    slot of its own, slots in path order; out and G then have D3 = sum of
+    2 l3 + 1 components."""
+
+    def __init__(self, l_in: int, l_sh: int, l_out: int, variant: int = 0):
+        self.l_in, self.l_sh, self.l_out, self.variant = l_in, l_sh, l_out, variant
+        self.paths = _cg.paths(l_in, l_sh, l_out, natural=(variant == 1))
         self.P = len(self.paths)
-        self.D1, self.D2, self.D3 = _cg.dim(l_in), _cg.dim(l_sh), _cg.dim(l_out)
+        self.D1, self.D2 = _cg.dim(l_in), _cg.dim(l_sh)
+        if variant == 0:
+            self.o3 = np.array([l3 * l3 for (_, _, l3) in self.paths], dtype=np.int32)
+            self.D3 = _cg.dim(l_out)
+        else:
+            sizes = [2 * l3 + 1 for (_, _, l3) in self.paths]
+            self.o3 = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int32) if sizes else \
+                np.zeros(0, dtype=np.int32)
+            self.D3 = int(sum(sizes))
         blocks = [_cg.real_cg(*p) for p in self.paths]
         self.blocks = blocks
         offs = np.zeros(self.P, dtype=np.int64)
@@ -83,6 +97,11 @@ class Problem:
         self.cg_flat = (np.concatenate([b.ravel() for b in blocks]) if blocks
                         else np.zeros(0)).astype(np.float64)
         self.l123 = np.array(self.paths, dtype=np.int32).reshape(-1, 3)
+
+    def oslice(self, p: int) -> slice:
+        """Output components of path p."""
+        l3 = self.paths[p][2]
+        return slice(int(self.o3[p]), int(self.o3[p]) + 2 * l3 + 1)
 
 
 def _ptr(a):
@@ -120,7 +139,7 @@ def materialised_fwd(prob: Problem, x, Y, w, row_ptr, senders):
         Cp = prob.blocks[p]
         xs = x[senders, l1 * l1:(l1 + 1) ** 2, :]
         ys = Y[:, l2 * l2:(l2 + 1) ** 2]
-        msg[:, l3 * l3:(l3 + 1) ** 2, :] += w[:, p, None, :] * np.einsum(
+        msg[:, prob.oslice(p), :] += w[:, p, None, :] * np.einsum(
             "abk,eac,eb->ekc", Cp, xs, ys, optimize=True)
     out = np.zeros((n, prob.D3, c))
     np.add.at(out, recv, msg)
@@ -143,7 +162,7 @@ def materialised_bwd(prob: Problem, x, Y, w, G, row_ptr, senders):
         Cp = prob.blocks[p]
         s1 = slice(l1 * l1, (l1 + 1) ** 2)
         s2 = slice(l2 * l2, (l2 + 1) ** 2)
-        s3 = slice(l3 * l3, (l3 + 1) ** 2)
+        s3 = prob.oslice(p)
         xs, ys, gs = x[senders, s1, :], Y[:, s2], gd[:, s3, :]
         dx_e[:, s1, :] += w[:, p, None, :] * np.einsum("abk,eb,ekc->eac", Cp, ys, gs, optimize=True)
         dw[:, p, :] = np.einsum("abk,eac,eb,ekc->ec", Cp, xs, ys, gs, optimize=True)
@@ -165,7 +184,7 @@ def fwd(prob: Problem, x, Y, w, row_ptr, senders, rows=None, n_threads=None):
     rows = _i32(np.arange(n) if rows is None else rows)
     out = np.zeros((rows.size, prob.D3, c))
     nt = n_threads or max_threads()
-    rc = lib().oracle_fwd(c, prob.D1, prob.D2, prob.D3, prob.P, _ptr(prob.l123),
+    rc = lib().oracle_fwd(c, prob.D1, prob.D2, prob.D3, prob.P, _ptr(prob.l123), _ptr(prob.o3),
                           _ptr(prob.cg_flat), _ptr(prob.cg_off), _ptr(x), _ptr(Y), _ptr(w),
                           _ptr(row_ptr), _ptr(senders), rows.size, _ptr(rows), _ptr(out), nt)
     if rc:
@@ -183,7 +202,7 @@ def bwd_dx(prob: Problem, Y, w, G, send_ptr, send_perm, send_recv, rows=None,
     rows = _i32(np.arange(n) if rows is None else rows)
     dx = np.zeros((rows.size, prob.D1, c))
     nt = n_threads or max_threads()
-    lib().oracle_bwd_dx(c, prob.D1, prob.D2, prob.D3, prob.P, _ptr(prob.l123),
+    lib().oracle_bwd_dx(c, prob.D1, prob.D2, prob.D3, prob.P, _ptr(prob.l123), _ptr(prob.o3),
                         _ptr(prob.cg_flat), _ptr(prob.cg_off), _ptr(Y), _ptr(w), _ptr(G),
                         _ptr(send_ptr), _ptr(send_perm), _ptr(send_recv),
                         rows.size, _ptr(rows), _ptr(dx), nt)
@@ -201,7 +220,7 @@ def bwd_edges(prob: Problem, x, Y, w, G, row_ptr, senders, rows=None, n_threads=
     dw = np.zeros((rows.size, prob.P, c))
     dY = np.zeros((rows.size, prob.D2))
     nt = n_threads or max_threads()
-    lib().oracle_bwd_edge(c, prob.D1, prob.D2, prob.D3, prob.P, _ptr(prob.l123),
+    lib().oracle_bwd_edge(c, prob.D1, prob.D2, prob.D3, prob.P, _ptr(prob.l123), _ptr(prob.o3),
                           _ptr(prob.cg_flat), _ptr(prob.cg_off), _ptr(x), _ptr(Y), _ptr(w),
                           _ptr(G), _ptr(senders), _ptr(recv), rows.size, _ptr(rows),
                           _ptr(dw), _ptr(dY), nt)
@@ -234,7 +253,7 @@ def materialised_double_bwd(prob: Problem, x, Y, w, G, ax, aw, aY, row_ptr, send
         Cp = prob.blocks[p]
         s1 = slice(l1 * l1, (l1 + 1) ** 2)
         s2 = slice(l2 * l2, (l2 + 1) ** 2)
-        s3 = slice(l3 * l3, (l3 + 1) ** 2)
+        s3 = prob.oslice(p)
         xs, axs, ys, ays, gs = x[senders, s1, :], ax[senders, s1, :], Y[:, s2], aY[:, s2], gd[:, s3, :]
         wp, awp = w[:, p, None, :], aw[:, p, None, :]
         # G enters every term of L2 linearly: gG = the three forwards with one

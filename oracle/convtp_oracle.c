@@ -26,7 +26,9 @@
  * at cg + cg_off[p], laid out [2l1+1][2l2+1][2l3+1].
  *
  * Component index d(l, m) = l*l + l + m; arrays are x[N][D1][C],
- * Y[E][D2], w[E][P][C], out/G[N][D3][C].  Every function evaluates only the
+ * Y[E][D2], w[E][P][C], out/G[N][D3][C].  Path p's output block starts at
+ * component o3[p]: l3*l3 when paths sharing l3 are summed, or the path's own
+ * slot when each path keeps its output (MACE's convolution).  Every function evaluates only the
  * rows (receivers, senders or edges) it is asked for, so large workloads can
  * be checked on samples.
  */
@@ -38,7 +40,7 @@
 #define IDX3(a, b, c, nb, nc) (((size_t)(a) * (nb) + (b)) * (nc) + (c))
 
 /* out[r][D3][C] for receiver rows[r] */
-int oracle_fwd(int C, int D1, int D2, int D3, int P, const int *l123,
+int oracle_fwd(int C, int D1, int D2, int D3, int P, const int *l123, const int *o3,
                const double *cg, const int64_t *cg_off,
                const float *x, const double *Y, const float *w,
                const int *row_ptr, const int *senders,
@@ -67,7 +69,7 @@ int oracle_fwd(int C, int D1, int D2, int D3, int P, const int *l123,
                             if (coef == 0.0) continue;
                             double t = coef * Y[(size_t)e * D2 + l2 * l2 + b];
                             const float *xs = x + IDX3(j, l1 * l1 + a, 0, D1, C);
-                            double *m = msg + (size_t)(l3 * l3 + k) * C;
+                            double *m = msg + (size_t)(o3[p] + k) * C;
                             for (int c = 0; c < C; ++c)
                                 m[c] += (double)wp[c] * t * (double)xs[c];
                         }
@@ -80,7 +82,7 @@ int oracle_fwd(int C, int D1, int D2, int D3, int P, const int *l123,
 }
 
 /* dx[r][D1][C] for sender rows[r], walking its out-edges via the transpose */
-int oracle_bwd_dx(int C, int D1, int D2, int D3, int P, const int *l123,
+int oracle_bwd_dx(int C, int D1, int D2, int D3, int P, const int *l123, const int *o3,
                   const double *cg, const int64_t *cg_off,
                   const double *Y, const float *w, const float *G,
                   const int *send_ptr, const int *send_perm, const int *send_recv,
@@ -104,7 +106,7 @@ int oracle_bwd_dx(int C, int D1, int D2, int D3, int P, const int *l123,
                             double coef = cp[(a * n2 + b) * n3 + q];
                             if (coef == 0.0) continue;
                             double t = coef * Y[(size_t)e * D2 + l2 * l2 + b];
-                            const float *g = G + IDX3(i, l3 * l3 + q, 0, D3, C);
+                            const float *g = G + IDX3(i, o3[p] + q, 0, D3, C);
                             double *d = o + (size_t)(l1 * l1 + a) * C;
                             for (int c = 0; c < C; ++c)
                                 d[c] += (double)wp[c] * t * (double)g[c];
@@ -116,7 +118,7 @@ int oracle_bwd_dx(int C, int D1, int D2, int D3, int P, const int *l123,
 }
 
 /* dw[r][P][C] and dY[r][D2] for edge rows[r]; recv[e] is the edge's receiver */
-int oracle_bwd_edge(int C, int D1, int D2, int D3, int P, const int *l123,
+int oracle_bwd_edge(int C, int D1, int D2, int D3, int P, const int *l123, const int *o3,
                     const double *cg, const int64_t *cg_off,
                     const float *x, const double *Y, const float *w, const float *G,
                     const int *senders, const int *recv,
@@ -142,7 +144,7 @@ int oracle_bwd_edge(int C, int D1, int D2, int D3, int P, const int *l123,
                         if (coef == 0.0) continue;
                         double yv = Y[(size_t)e * D2 + l2 * l2 + b];
                         const float *xs = x + IDX3(j, l1 * l1 + a, 0, D1, C);
-                        const float *g = G + IDX3(i, l3 * l3 + q, 0, D3, C);
+                        const float *g = G + IDX3(i, o3[p] + q, 0, D3, C);
                         double sy = 0.0;
                         for (int c = 0; c < C; ++c) {
                             double xg = (double)xs[c] * (double)g[c];

@@ -16,7 +16,7 @@ STATUS_NAMES = {0: "CTP_OK", 1: "CTP_EINVAL", 2: "CTP_EUNSUPPORTED", 3: "CTP_EAL
                 4: "CTP_EHIP", 5: "CTP_EGRAPH"}
 
 # Every symbol include/convtp.h declares.
-EXPORTS = ("conv_tp_num_paths", "conv_tp_paths", "conv_tp_coupling", "conv_tp_fwd", "conv_tp_bwd",
+EXPORTS = ("conv_tp_num_paths", "conv_tp_paths", "conv_tp_layout", "conv_tp_coupling", "conv_tp_fwd", "conv_tp_bwd",
            "conv_tp_bwd_bwd",
            "conv_tp_sh", "conv_tp_sh_bwd", "conv_tp_build_transpose", "conv_tp_check_graph",
            "conv_tp_node_fwd", "conv_tp_node_bwd", "conv_tp_stream_probe", "conv_tp_last_error",
@@ -27,7 +27,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("n_nodes", ctypes.c_int32), ("n_edges", ctypes.c_int32),
                 ("channels", ctypes.c_int32), ("l_in", ctypes.c_int32),
                 ("l_sh", ctypes.c_int32), ("l_out", ctypes.c_int32),
-                ("y_mode", ctypes.c_int32), ("algo", ctypes.c_int32)]
+                ("y_mode", ctypes.c_int32), ("algo", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 class NodeProblem(ctypes.Structure):
@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         "conv_tp_num_paths": ([i32, i32, i32], i32),
         "conv_tp_paths": ([i32, i32, i32, vp], i32),
         "conv_tp_coupling": ([i32, i32, i32, vp], i32),
+        "conv_tp_layout": ([i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), vp], i32),
         "conv_tp_fwd": ([pp, vp, vp, vp, vp, vp, vp, vp], i32),
         "conv_tp_bwd": ([pp] + [vp] * 13, i32),
         "conv_tp_bwd_bwd": ([pp] + [vp] * 17, i32),

@@ -73,14 +73,16 @@ int check_problem(const conv_tp_problem* pr, Shape* s) {
         return fail(CTP_EUNSUPPORTED, "degrees (%d,%d,%d) must be equal in this build", pr->l_in, pr->l_sh, pr->l_out);
     if (pr->y_mode != 0 && pr->y_mode != 1) return fail(CTP_EINVAL, "y_mode = %d not 0 or 1", pr->y_mode);
     if (pr->algo != 0 && pr->algo != 1) return fail(CTP_EINVAL, "algo = %d not 0 or 1", pr->algo);
+    if (pr->variant != ctp::kVariantSummed && pr->variant != ctp::kVariantSlots)
+        return fail(CTP_EINVAL, "variant = %d not 0 or 1", pr->variant);
     if (pr->n_nodes == 0 && pr->n_edges > 0) return fail(CTP_EGRAPH, "edges without nodes");
     s->N = pr->n_nodes;
     s->E = pr->n_edges;
     s->C = pr->channels;
     s->D1 = ctp::dim_of(pr->l_in);
     s->D2 = ctp::dim_of(pr->l_sh);
-    s->D3 = ctp::dim_of(pr->l_out);
-    s->P = ctp::num_paths(pr->l_in, pr->l_sh, pr->l_out);
+    s->D3 = ctp::out_dim(pr->l_in, pr->l_sh, pr->l_out, pr->variant);   // out and grad_out components
+    s->P = ctp::num_paths(pr->l_in, pr->l_sh, pr->l_out, pr->variant);
     s->S = pr->y_mode ? 3 : s->D2;
     return CTP_OK;
 }
@@ -93,6 +95,7 @@ ctp::LaunchArgs base_args(const conv_tp_problem* pr) {
     a.C = pr->channels;
     a.algo = pr->algo;
     a.vec_mode = pr->y_mode;
+    a.variant = pr->variant;
     return a;
 }
 
@@ -103,14 +106,16 @@ std::unordered_map<int, unsigned long long*> g_bad_buf;   // per-device counter 
 
 namespace ctp {
 
-int host_num_paths(int l1, int l2, int l3) { return num_paths(l1, l2, l3); }
+int host_num_paths(int l1, int l2, int l3, int variant) { return num_paths(l1, l2, l3, variant); }
 
-int host_paths(int l_in, int l_sh, int l_out, int32_t* l123) {
+int host_out_dim(int l1, int l2, int l3, int variant) { return out_dim(l1, l2, l3, variant); }
+
+int host_paths(int l_in, int l_sh, int l_out, int32_t* l123, int variant) {
     int n = 0;
     for (int a = 0; a <= l_in; ++a)
         for (int b = 0; b <= l_sh; ++b)
             for (int c = 0; c <= l_out; ++c)
-                if (triangle(a, b, c)) {
+                if (path_ok(a, b, c, variant)) {
                     l123[3 * n] = a;
                     l123[3 * n + 1] = b;
                     l123[3 * n + 2] = c;
@@ -132,7 +137,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 100; }
+int32_t conv_tp_version(void) { return 101; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
@@ -148,6 +153,20 @@ int32_t conv_tp_paths(int32_t l_in, int32_t l_sh, int32_t l_out, int32_t* l123) 
     if (int r = check_degree(l_out, "l_out")) return r;
     if (l123 == nullptr) return fail(CTP_EINVAL, "l123 is null");
     ctp::host_paths(l_in, l_sh, l_out, l123);
+    return ok();
+}
+
+int32_t conv_tp_layout(int32_t variant, int32_t l_in, int32_t l_sh, int32_t l_out, int32_t* n_paths,
+                       int32_t* out_dim, int32_t* l123) {
+    if (variant != ctp::kVariantSummed && variant != ctp::kVariantSlots)
+        return fail(CTP_EINVAL, "variant = %d not 0 or 1", variant);
+    if (int r = check_degree(l_in, "l_in")) return r;
+    if (int r = check_degree(l_sh, "l_sh")) return r;
+    if (int r = check_degree(l_out, "l_out")) return r;
+    if (n_paths == nullptr || out_dim == nullptr) return fail(CTP_EINVAL, "n_paths or out_dim is null");
+    *n_paths = ctp::host_num_paths(l_in, l_sh, l_out, variant);
+    *out_dim = ctp::host_out_dim(l_in, l_sh, l_out, variant);
+    if (l123 != nullptr) ctp::host_paths(l_in, l_sh, l_out, l123, variant);
     return ok();
 }
 
@@ -226,6 +245,8 @@ int32_t conv_tp_bwd_bwd(const conv_tp_problem* prob, const float* grad_out, cons
     if (int r = check_problem(prob, &s)) return r;
     if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the double backward has only the deterministic algorithm");
     if (prob->y_mode != 0) return fail(CTP_EUNSUPPORTED, "the double backward takes Y (y_mode 0)");
+    if (prob->variant != ctp::kVariantSummed)
+        return fail(CTP_EUNSUPPORTED, "the double backward is built for variant 0 (summed outputs)");
     if (!ctp::dd_supports_channels(prob->channels))
         return fail(CTP_EUNSUPPORTED, "double backward needs C <= 512, got %d", prob->channels);
     if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;

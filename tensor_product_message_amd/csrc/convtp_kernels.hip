@@ -40,6 +40,14 @@ template <> __device__ __forceinline__ const SlotDev* slot_tab<0>() { return kSl
 template <> __device__ __forceinline__ const SlotDev* slot_tab<1>() { return kSlot1.s; }
 template <> __device__ __forceinline__ const SlotDev* slot_tab<2>() { return kSlot2.s; }
 template <> __device__ __forceinline__ const SlotDev* slot_tab<3>() { return kSlot3.s; }
+__constant__ SlotTab<0, kVariantSlots> kSlotM0 = make_slot_tab<0, kVariantSlots>();
+__constant__ SlotTab<1, kVariantSlots> kSlotM1 = make_slot_tab<1, kVariantSlots>();
+__constant__ SlotTab<2, kVariantSlots> kSlotM2 = make_slot_tab<2, kVariantSlots>();
+__constant__ SlotTab<3, kVariantSlots> kSlotM3 = make_slot_tab<3, kVariantSlots>();
+template <> __device__ __forceinline__ const SlotDev* slot_tab<0, kVariantSlots>() { return kSlotM0.s; }
+template <> __device__ __forceinline__ const SlotDev* slot_tab<1, kVariantSlots>() { return kSlotM1.s; }
+template <> __device__ __forceinline__ const SlotDev* slot_tab<2, kVariantSlots>() { return kSlotM2.s; }
+template <> __device__ __forceinline__ const SlotDev* slot_tab<3, kVariantSlots>() { return kSlotM3.s; }
 __device__ __forceinline__ const ShTab& sh_tab() { return kShTab; }
 
 constexpr int kMaxThreads = 256;     // forward workgroups
@@ -67,10 +75,10 @@ __device__ __forceinline__ void stage_sh(float* sY, const float* __restrict__ yv
 }
 
 // T_{p,e} for all paths into sT, lane-parallel over the slots.
-template <int L>
+template <int L, int V>
 __device__ __forceinline__ void build_T(float* sT, const float* sY, int tid, int nth) {
-    constexpr int NT = Spec<L, L, L>::NT;
-    const SlotDev* tab = slot_tab<L>();
+    constexpr int NT = Spec<L, L, L, V>::NT;
+    const SlotDev* tab = slot_tab<L, V>();
     for (int t = tid; t < NT; t += nth) {
         const SlotDev s = tab[t];
         sT[t] = s.c1 * sY[s.yy & 0xff] + s.c2 * sY[s.yy >> 8];
@@ -79,13 +87,13 @@ __device__ __forceinline__ void build_T(float* sT, const float* sY, int tid, int
 
 // acc[l3 m3] += sum_p w_p * (T_p^T x[l1])[m3] for one edge and CPL channels.
 template <class S, int CPL>
-__device__ __forceinline__ void edge_forward(float (&acc)[S::D3][CPL], const float (&xv)[S::D1][CPL],
+__device__ __forceinline__ void edge_forward(float (&acc)[S::DO][CPL], const float (&xv)[S::D1][CPL],
                                              const float (&wv)[S::P][CPL], const float* sT) {
     static_for<S::P>([&](auto pI) __attribute__((always_inline)) {
         constexpr int p = decltype(pI)::value;
         constexpr PathL q = S::paths[p];
         constexpr int n1 = 2 * q.l1 + 1, n3 = 2 * q.l3 + 1;
-        constexpr int o1 = q.l1 * q.l1, o3 = q.l3 * q.l3;
+        constexpr int o1 = q.l1 * q.l1, o3 = S::out_off[p];   // o3: first output component of path p
         constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
         if constexpr (n1 <= n3) {
             // scale x by w first: n1 products, then one FMA per slot
@@ -153,14 +161,14 @@ constexpr bool last_path_of_l1(int p) {
 
 // Path loop of one edge with refills for the next edge.
 template <class S, int CPL>
-__device__ __forceinline__ void edge_forward_refill(float (&acc)[S::D3][CPL], float (&xv)[S::D1][CPL],
+__device__ __forceinline__ void edge_forward_refill(float (&acc)[S::DO][CPL], float (&xv)[S::D1][CPL],
                                                     float (&wv)[S::P][CPL], const float* sT, rsrc_t nx,
                                                     rsrc_t nw, uint32_t nvoff, int C) {
     static_for<S::P>([&](auto pI) __attribute__((always_inline)) {
         constexpr int p = decltype(pI)::value;
         constexpr PathL q = S::paths[p];
         constexpr int n1 = 2 * q.l1 + 1, n3 = 2 * q.l3 + 1;
-        constexpr int o1 = q.l1 * q.l1, o3 = q.l3 * q.l3;
+        constexpr int o1 = q.l1 * q.l1, o3 = S::out_off[p];   // o3: first output component of path p
         constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
         if constexpr (n1 <= n3) {
             float xs[n1][CPL];
@@ -212,12 +220,12 @@ __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::D3][CPL], fl
     });
 }
 
-template <int L, int CPL, bool VEC>
+template <int L, int CPL, bool VEC, int V>
 __global__ void __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(FWD_WPE, 8)))
 k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, const float* __restrict__ w,
           const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ out) {
-    using S = Spec<L, L, L>;
-    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
+    using S = Spec<L, L, L, V>;
+    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::DO, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
     __shared__ __attribute__((aligned(16))) float sT[2][NTP];
     __shared__ float sY[2][16];
     __shared__ SlotDev sTab[NT];
@@ -237,7 +245,7 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
     const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
     if (e0 < e1) {
         {
-            const SlotDev* tab = slot_tab<L>();
+            const SlotDev* tab = slot_tab<L, V>();
             for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
         }
         float xv[D1][CPL], wv[P][CPL];
@@ -245,7 +253,7 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
         const float y0 = sh_value<D2, VEC>(yv, e0, tid);
         if (tid < D2) sY[0][tid] = y0;
         __syncthreads();
-        build_T_lds<L>(sT[0], sY[0], sTab, tid, nth);
+        build_T_lds<L, V>(sT[0], sY[0], sTab, tid, nth);
         __syncthreads();
         for (int e = e0; e < e1; ++e) {
             const int buf = (e - e0) & 1;
@@ -260,7 +268,7 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
             if (has_next) {
                 if (tid < D2) sY[buf ^ 1][tid] = ynext;
                 __syncthreads();
-                build_T_lds<L>(sT[buf ^ 1], sY[buf ^ 1], sTab, tid, nth);
+                build_T_lds<L, V>(sT[buf ^ 1], sY[buf ^ 1], sTab, tid, nth);
                 __syncthreads();
             }
         }
@@ -278,13 +286,13 @@ __global__ void k_zero(float* __restrict__ p, long n) {
     for (; k < n; k += stride) p[k] = 0.0f;
 }
 
-template <int L, int CPL, bool VEC>
+template <int L, int CPL, bool VEC, int V>
 __global__ void __launch_bounds__(kMaxThreads)
 k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __restrict__ yv,
              const float* __restrict__ w, const int* __restrict__ row_ptr, const int* __restrict__ senders,
              float* __restrict__ out) {
-    using S = Spec<L, L, L>;
-    constexpr int D2 = S::D2, D3 = S::D3, NTP = (S::NT + 3) & ~3;
+    using S = Spec<L, L, L, V>;
+    constexpr int D2 = S::D2, D3 = S::DO, NTP = (S::NT + 3) & ~3;
     __shared__ __attribute__((aligned(16))) float sT[NTP];
     __shared__ float sY[16];
 
@@ -306,7 +314,7 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
     load_edge_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, voff);
     stage_sh<D2, VEC>(sY, yv, e, tid);
     __syncthreads();
-    build_T<L>(sT, sY, tid, nth);
+    build_T<L, V>(sT, sY, tid, nth);
     __syncthreads();
     float acc[D3][CPL];
 #pragma unroll
@@ -335,26 +343,29 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
 
 // G row of receiver i and w row of edge e, CPL channels per lane.
 template <class S, int CPL>
-__device__ __forceinline__ void load_bwd_operands(float (&gv)[S::D3][CPL], float (&wv)[S::P][CPL],
+__device__ __forceinline__ void load_bwd_operands(float (&gv)[S::DO][CPL], float (&wv)[S::P][CPL],
                                                   const float* __restrict__ G, const float* __restrict__ w, long i,
                                                   long e, int C, uint32_t voff) {
-    const rsrc_t gr = make_row(G + i * S::D3 * C, (long)S::D3 * C);
+    const rsrc_t gr = make_row(G + i * S::DO * C, (long)S::DO * C);
     const rsrc_t wr = make_row(w + e * S::P * C, (long)S::P * C);
     const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
 #pragma unroll
-    for (int d = 0; d < S::D3; ++d) bload<CPL>(gr, voff, (uint32_t)d * c4, gv[d]);
+    for (int d = 0; d < S::DO; ++d) bload<CPL>(gr, voff, (uint32_t)d * c4, gv[d]);
 #pragma unroll
     for (int p = 0; p < S::P; ++p) bload<CPL, kStream>(wr, voff, (uint32_t)p * c4, wv[p]);
 }
 
-template <int L, int CPL, bool VEC>
-__global__ void __launch_bounds__(kBwdMaxThreads) __attribute__((amdgpu_waves_per_eu(BWD_WPE, 8)))
+// With one G slot per path (variant 1) the G row alone is D_out registers per
+// channel, so that variant may take two waves per SIMD instead of spilling.
+template <int L, int CPL, bool VEC, int V>
+__global__ void __launch_bounds__(kBwdMaxThreads)
+__attribute__((amdgpu_waves_per_eu(V == kVariantSlots ? 2 : BWD_WPE, 8)))
 k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ yv,
              const float* __restrict__ w, const int* __restrict__ send_ptr, const int* __restrict__ send_perm,
              const int* __restrict__ send_recv, float* __restrict__ dx, float* __restrict__ dw,
              float* __restrict__ dyv) {
-    using S = Spec<L, L, L>;
-    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
+    using S = Spec<L, L, L, V>;
+    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::DO, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
     __shared__ __attribute__((aligned(16))) float sT[2][NTP];
     __shared__ float sY[2][16];
     __shared__ float sRed[kBwdMaxThreads / 64][16];
@@ -380,7 +391,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
     const int k0 = send_ptr[j], k1 = send_ptr[j + 1];
     if (k0 < k1) {
         {
-            const SlotDev* tab = slot_tab<L>();
+            const SlotDev* tab = slot_tab<L, V>();
             for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
         }
         float gv[D3][CPL], wv[P][CPL];
@@ -389,7 +400,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
         load_bwd_operands<S, CPL>(gv, wv, G, w, send_recv[k0], e, C, voff);
         if (tid < D2) sY[0][tid] = y0;
         __syncthreads();
-        build_T_lds<L>(sT[0], sY[0], sTab, tid, nth);
+        build_T_lds<L, V>(sT[0], sY[0], sTab, tid, nth);
         __syncthreads();
 
         // Per out-edge k: compute with T(k) and the rows already in registers;
@@ -408,14 +419,13 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
             float dya[16];
 #pragma unroll
             for (int d = 0; d < 16; ++d) dya[d] = 0.0f;
-            static_for<L + 1>([&](auto l1I) __attribute__((always_inline)) {
-                constexpr int l1 = decltype(l1I)::value;
-                static_for<L + 1>([&](auto l3I) __attribute__((always_inline)) {
-                    constexpr int l3 = decltype(l3I)::value;
-                    constexpr PairPaths pp = pair_paths<S>(l1, l3);
-                    if constexpr (pp.n > 0) {
+            static_for<S::NG>([&](auto gI) __attribute__((always_inline)) {
+                constexpr PathGroup pp = S::groups[decltype(gI)::value];
+                constexpr int l1 = pp.l1, l3 = pp.l3;
+                {
+                    {
                         constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
-                        constexpr int o1 = l1 * l1, o3 = l3 * l3;
+                        constexpr int o1 = l1 * l1, o3 = pp.o3;   // o3: the group's block of G
                         // (a) v_p = T_p^T g, dw_p = x . v_p, dx += w_p v_p
                         static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
                             constexpr int p = pp.p[decltype(kI)::value];
@@ -491,7 +501,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
                         });
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                });
+                }
             });
 
             // rows of the next edge into the registers just freed (unconditional:
@@ -517,7 +527,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
             if (sum16_holder(ln)) sRed[tt >> 6][sum16_index(ln)] = r;
             if (has_next && tt < D2) sY[buf ^ 1][tt] = ynext;
             __syncthreads();
-            if (has_next) build_T_lds<L>(sT[buf ^ 1], sY[buf ^ 1], sTab, tt, nth);
+            if (has_next) build_T_lds<L, V>(sT[buf ^ 1], sY[buf ^ 1], sTab, tt, nth);
             float tot = 0.0f;
             if (tt < D2) {
                 tot = sRed[0][tt];
@@ -623,50 +633,56 @@ ChanMap chan_map(int C, int max_waves, long rows) {
     return m;
 }
 
-template <int L, int CPL>
+template <int L, int CPL, int V>
 hipError_t fwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
     dim3 block(64 * m.waves);
     if (a.algo == 0) {
         dim3 grid(a.n_nodes, m.tiles);
         if (a.vec_mode)
-            hipLaunchKernelGGL((k_fwd_csr<L, CPL, true>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
+            hipLaunchKernelGGL((k_fwd_csr<L, CPL, true, V>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
                                a.senders, a.out);
         else
-            hipLaunchKernelGGL((k_fwd_csr<L, CPL, false>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
+            hipLaunchKernelGGL((k_fwd_csr<L, CPL, false, V>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
                                a.senders, a.out);
     } else {
-        const long n = (long)a.n_nodes * Spec<L, L, L>::D3 * a.C;
+        const long n = (long)a.n_nodes * Spec<L, L, L, V>::DO * a.C;
         hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, st, a.out, n);
         if (a.n_edges > 0) {
             dim3 grid(a.n_edges, m.tiles);
             if (a.vec_mode)
-                hipLaunchKernelGGL((k_fwd_atomic<L, CPL, true>), grid, block, 0, st, a.n_nodes, a.C, a.x, a.y,
+                hipLaunchKernelGGL((k_fwd_atomic<L, CPL, true, V>), grid, block, 0, st, a.n_nodes, a.C, a.x, a.y,
                                    a.w, a.row_ptr, a.senders, a.out);
             else
-                hipLaunchKernelGGL((k_fwd_atomic<L, CPL, false>), grid, block, 0, st, a.n_nodes, a.C, a.x, a.y,
+                hipLaunchKernelGGL((k_fwd_atomic<L, CPL, false, V>), grid, block, 0, st, a.n_nodes, a.C, a.x, a.y,
                                    a.w, a.row_ptr, a.senders, a.out);
         }
     }
     return hipGetLastError();
 }
 
-template <int L, int CPL>
+template <int L, int CPL, int V>
 hipError_t bwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
     static_assert(CPL == 1, "the backward maps one channel per lane");
     dim3 grid(a.n_nodes), block(64 * m.waves);
     if (a.vec_mode)
-        hipLaunchKernelGGL((k_bwd_sender<L, CPL, true>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+        hipLaunchKernelGGL((k_bwd_sender<L, CPL, true, V>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
                            a.send_ptr, a.send_perm, a.send_recv, a.dx, a.dw, a.dy);
     else
-        hipLaunchKernelGGL((k_bwd_sender<L, CPL, false>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+        hipLaunchKernelGGL((k_bwd_sender<L, CPL, false, V>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
                            a.send_ptr, a.send_perm, a.send_recv, a.dx, a.dw, a.dy);
     return hipGetLastError();
 }
 
 template <int L>
 hipError_t fwd_L(const LaunchArgs& a, hipStream_t st) {
-    const ChanMap m = chan_map(a.C, kMaxThreads / 64, a.algo == 0 ? (long)a.n_nodes : a.n_edges);
-    return m.cpl == 2 ? fwd_dispatch<L, 2>(a, m, st) : fwd_dispatch<L, 1>(a, m, st);
+    ChanMap m = chan_map(a.C, kMaxThreads / 64, a.algo == 0 ? (long)a.n_nodes : a.n_edges);
+    if (a.variant == kVariantSlots) {
+        // one output slot per path: the accumulators alone take D_out registers
+        // per channel, so one channel per lane
+        if (m.cpl == 2) m = chan_map(a.C, kMaxThreads / 64, 0);
+        return fwd_dispatch<L, 1, kVariantSlots>(a, m, st);
+    }
+    return m.cpl == 2 ? fwd_dispatch<L, 2, kVariantSummed>(a, m, st) : fwd_dispatch<L, 1, kVariantSummed>(a, m, st);
 }
 
 ChanMap bwd_chan_map(int C) {
@@ -679,7 +695,8 @@ ChanMap bwd_chan_map(int C) {
 
 template <int L>
 hipError_t bwd_L(const LaunchArgs& a, hipStream_t st) {
-    return bwd_dispatch<L, 1>(a, bwd_chan_map(a.C), st);
+    if (a.variant == kVariantSlots) return bwd_dispatch<L, 1, kVariantSlots>(a, bwd_chan_map(a.C), st);
+    return bwd_dispatch<L, 1, kVariantSummed>(a, bwd_chan_map(a.C), st);
 }
 
 }  // namespace

@@ -84,21 +84,21 @@ struct SlotDev {
     float c1, c2;
 };
 
-template <int L>
+template <int L, int V = kVariantSummed>
 struct SlotTab {
-    SlotDev s[Spec<L, L, L>::NT];
+    SlotDev s[Spec<L, L, L, V>::NT];
 };
 
-template <int L>
-constexpr SlotTab<L> make_slot_tab() {
-    using S = Spec<L, L, L>;
-    SlotTab<L> r{};
+template <int L, int V = kVariantSummed>
+constexpr SlotTab<L, V> make_slot_tab() {
+    using S = Spec<L, L, L, V>;
+    SlotTab<L, V> r{};
     for (int t = 0; t < S::NT; ++t)
         r.s[t] = SlotDev{S::slots[t].y1 | (S::slots[t].y2 << 8), S::slots[t].c1, S::slots[t].c2};
     return r;
 }
 
-template <int L>
+template <int L, int V = kVariantSummed>
 __device__ __forceinline__ const SlotDev* slot_tab();
 
 // ------------------------------------------------------------ real spherical harmonics
@@ -387,9 +387,9 @@ __device__ __forceinline__ float sh_load(const float* __restrict__ yv, long e, i
     }
 }
 
-template <int L>
+template <int L, int V = kVariantSummed>
 __device__ __forceinline__ void build_T_lds(float* sT, const float* sY, const SlotDev* tab, int tid, int nth) {
-    constexpr int NT = Spec<L, L, L>::NT;
+    constexpr int NT = Spec<L, L, L, V>::NT;
     for (int t = tid; t < NT; t += nth) {
         const SlotDev s = tab[t];
         sT[t] = s.c1 * sY[s.yy & 0xff] + s.c2 * sY[s.yy >> 8];

@@ -12,6 +12,7 @@ struct LaunchArgs {
     int n_nodes, n_edges, C;
     int algo;              // 0: CSR deterministic, 1: edge-parallel atomic (forward only)
     int vec_mode;          // 0: Y[E][D] given, 1: vec[E][3] given
+    int variant;           // 0: all paths, same-l3 sums; 1: natural-parity paths, one output slot each
     const float* x;        // [N][D][C]
     const float* y;        // Y[E][D] or vec[E][3]
     const float* w;        // [E][P][C]

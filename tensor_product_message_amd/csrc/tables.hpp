@@ -32,12 +32,34 @@ constexpr bool triangle(int a, int b, int c) {
     return (a - b <= c && b - a <= c) && c <= a + b;
 }
 
-constexpr int num_paths(int L1, int L2, int L3) {
+// Path variants.  0: every triangle-allowed path, paths sharing l3 summed
+// into one output block.  1 (MACE's convolution): only natural-parity paths
+// (l1 + l2 + l3 even), each with an output slot of its own.
+constexpr int kVariantSummed = 0;
+constexpr int kVariantSlots = 1;
+
+constexpr bool path_ok(int a, int b, int c, int V) {
+    return triangle(a, b, c) && (V == kVariantSummed || (a + b + c) % 2 == 0);
+}
+
+constexpr int num_paths(int L1, int L2, int L3, int V = kVariantSummed) {
     int n = 0;
     for (int a = 0; a <= L1; ++a)
         for (int b = 0; b <= L2; ++b)
             for (int c = 0; c <= L3; ++c)
-                if (triangle(a, b, c)) ++n;
+                if (path_ok(a, b, c, V)) ++n;
+    return n;
+}
+
+// Output components per channel: (L3+1)^2 summed, sum of 2 l3 + 1 over the
+// paths with slots.
+constexpr int out_dim(int L1, int L2, int L3, int V) {
+    if (V == kVariantSummed) return dim_of(L3);
+    int n = 0;
+    for (int a = 0; a <= L1; ++a)
+        for (int b = 0; b <= L2; ++b)
+            for (int c = 0; c <= L3; ++c)
+                if (path_ok(a, b, c, V)) n += 2 * c + 1;
     return n;
 }
 
@@ -146,10 +168,18 @@ struct CgNz {
     float c;
 };
 
-template <int L1, int L2, int L3>
+// A set of paths that read the same block of G in the backward: for summed
+// outputs all paths with the same (l1, l3) (block l3), for slots one path.
+struct PathGroup {
+    int l1, l3, o3, n;
+    int p[kMaxL + 1];
+};
+
+template <int L1, int L2, int L3, int V = kVariantSummed>
 struct Spec {
     static constexpr int D1 = dim_of(L1), D2 = dim_of(L2), D3 = dim_of(L3);
-    static constexpr int P = num_paths(L1, L2, L3);
+    static constexpr int P = num_paths(L1, L2, L3, V);
+    static constexpr int DO = out_dim(L1, L2, L3, V);   // output (and G) components
 
     static constexpr std::array<PathL, P> make_paths() {
         std::array<PathL, P> r{};
@@ -157,10 +187,56 @@ struct Spec {
         for (int a = 0; a <= L1; ++a)
             for (int b = 0; b <= L2; ++b)
                 for (int c = 0; c <= L3; ++c)
-                    if (triangle(a, b, c)) r[n++] = PathL{a, b, c};
+                    if (path_ok(a, b, c, V)) r[n++] = PathL{a, b, c};
         return r;
     }
     static constexpr std::array<PathL, P> paths = make_paths();
+
+    // First output component of each path's contribution.
+    static constexpr std::array<int, P> make_out_off() {
+        std::array<int, P> r{};
+        int o = 0;
+        for (int p = 0; p < P; ++p) {
+            r[p] = V == kVariantSummed ? paths[p].l3 * paths[p].l3 : o;
+            o += 2 * paths[p].l3 + 1;
+        }
+        return r;
+    }
+    static constexpr std::array<int, P> out_off = make_out_off();
+
+    static constexpr int count_groups() {
+        if (V != kVariantSummed) return P;
+        int n = 0;
+        for (int a = 0; a <= L1; ++a)
+            for (int c = 0; c <= L3; ++c) {
+                bool any = false;
+                for (int p = 0; p < P; ++p)
+                    if (paths[p].l1 == a && paths[p].l3 == c) any = true;
+                if (any) ++n;
+            }
+        return n;
+    }
+    static constexpr int NG = count_groups();
+
+    // Groups in the order the backward walks them: (l1, l3) with l1 outer for
+    // summed outputs, path order for slots.
+    static constexpr std::array<PathGroup, NG> make_groups() {
+        std::array<PathGroup, NG> r{};
+        int n = 0;
+        if (V != kVariantSummed) {
+            for (int p = 0; p < P; ++p) r[n++] = PathGroup{paths[p].l1, paths[p].l3, out_off[p], 1, {p, 0, 0, 0}};
+            return r;
+        }
+        for (int a = 0; a <= L1; ++a)
+            for (int c = 0; c <= L3; ++c) {
+                PathGroup g{a, c, c * c, 0, {0, 0, 0, 0}};
+                for (int p = 0; p < P; ++p)
+                    if (paths[p].l1 == a && paths[p].l3 == c) g.p[g.n++] = p;
+                if (g.n > 0) r[n++] = g;
+            }
+        return r;
+    }
+    static constexpr std::array<PathGroup, NG> groups = make_groups();
 
     static constexpr int count_nz() {
         int n = 0;
@@ -254,8 +330,9 @@ struct Spec {
 };
 
 // Host-side lookups for the C ABI (runtime degrees).
-int host_num_paths(int l1, int l2, int l3);
-int host_paths(int l_in, int l_sh, int l_out, int32_t* l123);
+int host_num_paths(int l1, int l2, int l3, int variant = kVariantSummed);
+int host_out_dim(int l1, int l2, int l3, int variant);
+int host_paths(int l_in, int l_sh, int l_out, int32_t* l123, int variant = kVariantSummed);
 int host_coupling(int l1, int l2, int l3, double* out);
 
 }  // namespace ctp

@@ -24,6 +24,7 @@ from ._capi import ConvTPError, Problem, check, lib  # noqa: F401
 
 Y_GIVEN, VEC_GIVEN = 0, 1
 ALGO_CSR, ALGO_ATOMIC = 0, 1
+SUMMED, SLOTS = 0, 1          # path variants (conv_tp_problem.variant)
 
 
 def _p(t):
@@ -69,6 +70,17 @@ def paths(l_in: int, l_sh: int = None, l_out: int = None):
     buf = np.zeros((n, 3), dtype=np.int32)
     check(lib().conv_tp_paths(l_in, l_sh, l_out, buf.ctypes.data_as(ctypes.c_void_p)))
     return [tuple(int(v) for v in r) for r in buf]
+
+
+def layout(lmax: int, variant: int = SUMMED):
+    """(paths, out_dim) of a variant: the path list in w's order and the
+    number of output components per channel."""
+    n, d = ctypes.c_int32(0), ctypes.c_int32(0)
+    check(lib().conv_tp_layout(variant, lmax, lmax, lmax, ctypes.byref(n), ctypes.byref(d), None))
+    buf = np.zeros((n.value, 3), dtype=np.int32)
+    check(lib().conv_tp_layout(variant, lmax, lmax, lmax, ctypes.byref(n), ctypes.byref(d),
+                               buf.ctypes.data_as(ctypes.c_void_p)))
+    return [tuple(int(v) for v in r) for r in buf], int(d.value)
 
 
 def coupling(l1: int, l2: int, l3: int) -> np.ndarray:
@@ -126,39 +138,45 @@ def check_graph(n_nodes: int, row_ptr: torch.Tensor, senders: torch.Tensor) -> i
     return int(bad.value)
 
 
-def _problem(n_nodes, n_edges, channels, lmax, y_mode, algo) -> Problem:
-    return Problem(n_nodes, n_edges, channels, lmax, lmax, lmax, y_mode, algo)
+def _problem(n_nodes, n_edges, channels, lmax, y_mode, algo, variant=SUMMED) -> Problem:
+    return Problem(n_nodes, n_edges, channels, lmax, lmax, lmax, y_mode, algo, variant)
 
 
-def _shapes(x, y_or_vec, w, graph, lmax, y_mode):
+def _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant=SUMMED):
     n, e = graph.n_nodes, graph.n_edges
     if x.dim() != 3:
         raise ValueError("x must be [N, D, C]")
     c = x.shape[2]
     _want(x, "x", (n, dim(lmax), c), device=graph.device)
     _want(y_or_vec, "y_or_vec", (e, dim(lmax) if y_mode == Y_GIVEN else 3), device=graph.device)
-    _want(w, "w", (e, num_paths(lmax), c), device=graph.device)
+    p = num_paths(lmax) if variant == SUMMED else len(layout(lmax, variant)[0])
+    _want(w, "w", (e, p, c), device=graph.device)
     return n, e, c
 
 
+def out_dim(lmax: int, variant: int = SUMMED) -> int:
+    return dim(lmax) if variant == SUMMED else layout(lmax, variant)[1]
+
+
 def conv_tp_fwd(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN, algo: int = ALGO_CSR,
-                out=None):
-    """out[N, D, C] = conv(x, Y or vec, w) on `graph` (see include/convtp.h)."""
-    n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode)
+                out=None, variant: int = SUMMED):
+    """out[N, D_out, C] = conv(x, Y or vec, w) on `graph` (see include/convtp.h)."""
+    n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant)
+    do = out_dim(lmax, variant)
     if out is None:
-        out = torch.empty((n, dim(lmax), c), dtype=torch.float32, device=x.device)
-    _want(out, "out", (n, dim(lmax), c), device=x.device)
-    prob = _problem(n, e, c, lmax, y_mode, algo)
+        out = torch.empty((n, do, c), dtype=torch.float32, device=x.device)
+    _want(out, "out", (n, do, c), device=x.device)
+    prob = _problem(n, e, c, lmax, y_mode, algo, variant)
     check(lib().conv_tp_fwd(ctypes.byref(prob), _p(x), _p(y_or_vec), _p(w), _p(graph.row_ptr),
                             _p(graph.senders), _p(out), _stream(x)))
     return out
 
 
 def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN,
-                dx=None, dw=None, dy=None):
+                dx=None, dw=None, dy=None, variant: int = SUMMED):
     """(dx, dw, dY or dvec) for upstream gradient grad_out (see include/convtp.h)."""
-    n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode)
-    _want(grad_out, "grad_out", (n, dim(lmax), c), device=x.device)
+    n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant)
+    _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
     send_ptr, send_perm, send_recv = graph.transpose
     dx = torch.empty_like(x) if dx is None else dx
     dw = torch.empty_like(w) if dw is None else dw
@@ -166,7 +184,7 @@ def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int =
     _want(dx, "dx", x.shape, device=x.device)
     _want(dw, "dw", w.shape, device=x.device)
     _want(dy, "dy", y_or_vec.shape, device=x.device)
-    prob = _problem(n, e, c, lmax, y_mode, ALGO_CSR)
+    prob = _problem(n, e, c, lmax, y_mode, ALGO_CSR, variant)
     check(lib().conv_tp_bwd(ctypes.byref(prob), _p(grad_out), _p(x), _p(y_or_vec), _p(w),
                             _p(graph.row_ptr), _p(graph.senders), _p(send_ptr), _p(send_perm),
                             _p(send_recv), _p(dx), _p(dw), _p(dy), _stream(x)))

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 100
+    assert L.conv_tp_version() == 101
 
 
 def test_paths_match_oracle(capi):
@@ -42,6 +42,22 @@ def test_paths_match_oracle(capi):
         assert t.num_paths(L) == len(cg.paths(L, L, L))
         assert t.paths(L) == cg.paths(L, L, L)
     assert t.paths(0, 3, 3) == cg.paths(0, 3, 3)
+
+
+def test_variant_layouts_match_oracle(capi):
+    import tensor_product_message_amd as t
+    from oracle import convtp as oc
+    for L in range(4):
+        for v in (0, 1):
+            ps, d = t.layout(L, v)
+            pr = oc.Problem(L, L, L, variant=v)
+            assert ps == pr.paths and d == pr.D3
+    L = capi.lib()
+    n, d = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert L.conv_tp_layout(2, 1, 1, 1, ctypes.byref(n), ctypes.byref(d), None) == capi.CTP_EINVAL
+    assert L.conv_tp_layout(1, 4, 4, 4, ctypes.byref(n), ctypes.byref(d), None) == capi.CTP_EUNSUPPORTED
+    assert L.conv_tp_layout(1, 1, 1, 1, None, ctypes.byref(d), None) == capi.CTP_EINVAL
+    assert _fwd(capi, _prob(capi, variant=3)) == capi.CTP_EINVAL
 
 
 def test_coupling_tables_match_oracle(capi):

@@ -65,16 +65,16 @@ def sh32(L, vec):
 # ------------------------------------------------------------ small workloads, full comparison
 
 
-def run_small(ctp, dev, d, L, y_mode, algo=0, bwd=True):
+def run_small(ctp, dev, d, L, y_mode, algo=0, bwd=True, variant=0):
     n, e = d["n_nodes"], d["n_edges"]
-    prob = oc.Problem(L, L, L)
+    prob = oc.Problem(L, L, L, variant=variant)
     vec = d["vec"]
     Y = sh32(L, vec)
     yin = Y if y_mode == 0 else vec
     g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
     x, w = T(d["x"], dev), T(d["w"], dev)
     yv = T(yin, dev)
-    out = ctp.conv_tp_fwd(x, yv, w, g, L, y_mode, algo)
+    out = ctp.conv_tp_fwd(x, yv, w, g, L, y_mode, algo, variant=variant)
     # oracle: Y mode sees the same fp32 Y; vec mode sees fp64 harmonics of the same vec
     Yref = Y.astype(np.float64) if y_mode == 0 else osh.real_sh(L, vec.astype(np.float64))
     ref = oc.fwd(prob, d["x"], Yref, d["w"], d["row_ptr"], d["senders"])
@@ -82,7 +82,7 @@ def run_small(ctp, dev, d, L, y_mode, algo=0, bwd=True):
     if not bwd:
         return
     G = T(d["grad_out"], dev)
-    dx, dw, dy = ctp.conv_tp_bwd(G, x, yv, w, g, L, y_mode)
+    dx, dw, dy = ctp.conv_tp_bwd(G, x, yv, w, g, L, y_mode, variant=variant)
     sp, pe, sr = og.transpose(n, d["row_ptr"], d["senders"])
     close("dx", host(dx), oc.bwd_dx(prob, Yref, d["w"], d["grad_out"], sp, pe, sr))
     dw_ref, dY_ref = oc.bwd_edges(prob, d["x"], Yref, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
@@ -436,3 +436,53 @@ def test_double_bwd_full_l3_sampled(ctp, dev):
     ei = torch.as_tensor(edges, device=dev)
     close("g_w[sample]", host(gw[ei]), dw1 + dw2)
     close("g_y[sample]", host(gy[ei]), dY1 + dY3)
+
+
+# ------------------------------------------------------------ MACE variant (natural parity, slots)
+
+
+def _variant_inputs(d, L):
+    """Resize w and grad_out of a summed-variant workload to the slot variant
+    (the generators draw the summed shapes; the extra values are simply not used)."""
+    pr = oc.Problem(L, L, L, variant=1)
+    rng = np.random.default_rng(d["n_nodes"] + 17)
+    d = dict(d)
+    d["w"] = rng.standard_normal((d["n_edges"], pr.P, d["x"].shape[2]), dtype=np.float32)
+    d["grad_out"] = rng.standard_normal((d["n_nodes"], pr.D3, d["x"].shape[2]), dtype=np.float32)
+    return d
+
+
+@pytest.mark.parametrize("n,c,L", [(90, 16, 1), (150, 48, 2), (100, 128, 3), (70, 64, 3), (60, 192, 3),
+                                   (40, 96, 0), (30, 512, 2)])
+@pytest.mark.parametrize("y_mode", [0, 1])
+def test_variant_slots_small(ctp, dev, n, c, L, y_mode):
+    d = _variant_inputs(gen.poisson_small(n, c, L, mean_deg=12.0, seed=n + c + L), L)
+    run_small(ctp, dev, d, L, y_mode, 0, bwd=True, variant=1)
+    run_small(ctp, dev, d, L, y_mode, 1, bwd=False, variant=1)
+
+
+def test_variant_slots_full_l3_sampled(ctp, dev):
+    """lmax=3, N=16384, C=128, Poisson(45), Y given, natural-parity paths with slots."""
+    n, c, L = 16384, 128, 3
+    d = gen.poisson_full(n, c, L, dev, seed=0, need_grad=False)
+    pr = oc.Problem(L, L, L, variant=1)
+    rp, s = d["row_ptr"], d["senders"]
+    e = len(s)
+    w = gen.normal_tensor((e, pr.P, c), 0, 21, dev)
+    G = gen.normal_tensor((n, pr.D3, c), 0, 23, dev)
+    Y = sh32(L, d["vec"])
+    g = ctp.Graph(n, T(rp, dev), T(s, dev))
+    out = ctp.conv_tp_fwd(d["x"], T(Y, dev), w, g, L, 0, variant=1)
+    dx, dw, dy = ctp.conv_tp_bwd(G, d["x"], T(Y, dev), w, g, L, 0, variant=1)
+    Yr = Y.astype(np.float64)
+    x_h, G_h = host(d["x"]), host(G)
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(n, 32, replace=False))
+    ri = torch.as_tensor(rows, device=dev)
+    close("out[sample]", host(out[ri]), _sub_fwd(pr, rp, s, Yr, w, x_h, rows))
+    close("dx[sample]", host(dx[ri]), _sub_dx(pr, rp, s, Yr, w, G_h, rows))
+    edges = np.sort(rng.choice(e, 128, replace=False))
+    dw_ref, dY_ref = _sub_edges(pr, rp, s, Yr, w, x_h, G_h, edges)
+    ei = torch.as_tensor(edges, device=dev)
+    close("dw[sample]", host(dw[ei]), dw_ref)
+    close("dY[sample]", host(dy[ei]), dY_ref)
