@@ -220,7 +220,11 @@ __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::DO][CPL], fl
     });
 }
 
-template <int L, int CPL, bool VEC, int V>
+// SPLIT (small grids): blockIdx.z picks one half of the row's edges, and the
+// two halves add their sums into a zeroed out with fp32 atomics.  With exactly
+// two addends onto zero the result is the same in either order, so the
+// output stays bitwise reproducible.
+template <int L, int CPL, bool VEC, int V, bool SPLIT>
 __global__ void __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(FWD_WPE, 8)))
 k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, const float* __restrict__ w,
           const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ out) {
@@ -242,7 +246,11 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[d][c] = 0.0f;
 
-    const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
+    int e0 = row_ptr[i], e1 = row_ptr[i + 1];
+    if constexpr (SPLIT) {
+        const int mid = e0 + (e1 - e0 + 1) / 2;
+        if (blockIdx.z == 0) e1 = mid; else e0 = mid;
+    }
     if (e0 < e1) {
         {
             const SlotDev* tab = slot_tab<L, V>();
@@ -273,9 +281,19 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
             }
         }
     }
-    const rsrc_t orow = make_row(out + (long)i * D3 * C, (long)D3 * C);
+    if constexpr (SPLIT) {
+        if (e0 < e1 && c0 < C) {
+            float* o = out + (long)i * D3 * C + c0;
 #pragma unroll
-    for (int d = 0; d < D3; ++d) bstore<CPL, kStream>(orow, voff, (uint32_t)(d * C * 4), acc[d]);
+            for (int d = 0; d < D3; ++d)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + 64 * c, acc[d][c]);
+        }
+    } else {
+        const rsrc_t orow = make_row(out + (long)i * D3 * C, (long)D3 * C);
+#pragma unroll
+        for (int d = 0; d < D3; ++d) bstore<CPL, kStream>(orow, voff, (uint32_t)(d * C * 4), acc[d]);
+    }
 }
 
 // ------------------------------------------------------------ K2: edge-parallel atomic forward (comparison)
@@ -357,7 +375,9 @@ __device__ __forceinline__ void load_bwd_operands(float (&gv)[S::DO][CPL], float
 
 // With one G slot per path (variant 1) the G row alone is D_out registers per
 // channel, so that variant may take two waves per SIMD instead of spilling.
-template <int L, int CPL, bool VEC, int V>
+// SPLIT (small grids): blockIdx.y picks one half of the sender's out-edges;
+// dx is added with fp32 atomics into a zeroed dx (two addends: order-free).
+template <int L, int CPL, bool VEC, int V, bool SPLIT>
 __global__ void __launch_bounds__(kBwdMaxThreads)
 __attribute__((amdgpu_waves_per_eu(V == kVariantSlots ? 2 : BWD_WPE, 8)))
 k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ yv,
@@ -388,7 +408,11 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
         }
     }
 
-    const int k0 = send_ptr[j], k1 = send_ptr[j + 1];
+    int k0 = send_ptr[j], k1 = send_ptr[j + 1];
+    if constexpr (SPLIT) {
+        const int mid = k0 + (k1 - k0 + 1) / 2;
+        if (blockIdx.y == 0) k1 = mid; else k0 = mid;
+    }
     if (k0 < k1) {
         {
             const SlotDev* tab = slot_tab<L, V>();
@@ -563,9 +587,19 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
         }
     }
 
-    const rsrc_t dxr = make_row(dx + (long)j * D1 * C, (long)D1 * C);
+    if constexpr (SPLIT) {
+        if (k0 < k1 && c0 < C) {
+            float* o = dx + (long)j * D1 * C + c0;
 #pragma unroll
-    for (int d = 0; d < D1; ++d) bstore<CPL, kStream>(dxr, voff, (uint32_t)(d * C * 4), dxa[d]);
+            for (int d = 0; d < D1; ++d)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + 64 * c, dxa[d][c]);
+        }
+    } else {
+        const rsrc_t dxr = make_row(dx + (long)j * D1 * C, (long)D1 * C);
+#pragma unroll
+        for (int d = 0; d < D1; ++d) bstore<CPL, kStream>(dxr, voff, (uint32_t)(d * C * 4), dxa[d]);
+    }
 }
 
 // ------------------------------------------------------------ standalone harmonics (vec -> Y, dY -> dvec)
@@ -633,17 +667,33 @@ ChanMap chan_map(int C, int max_waves, long rows) {
     return m;
 }
 
+// Grids with fewer waves than 4 per SIMD split every edge list in two (SPLIT).
+constexpr long kSplitBelowWaves = 4L * 1024;
+
+template <int L, int CPL, int V, bool SPLIT>
+hipError_t fwd_csr_launch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
+    const dim3 grid(a.n_nodes, m.tiles, SPLIT ? 2 : 1), block(64 * m.waves);
+    if (SPLIT) {
+        const long n = (long)a.n_nodes * Spec<L, L, L, V>::DO * a.C;
+        hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, st, a.out, n);
+    }
+    if (a.vec_mode)
+        hipLaunchKernelGGL((k_fwd_csr<L, CPL, true, V, SPLIT>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
+                           a.senders, a.out);
+    else
+        hipLaunchKernelGGL((k_fwd_csr<L, CPL, false, V, SPLIT>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
+                           a.senders, a.out);
+    return hipGetLastError();
+}
+
 template <int L, int CPL, int V>
 hipError_t fwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
     dim3 block(64 * m.waves);
     if (a.algo == 0) {
-        dim3 grid(a.n_nodes, m.tiles);
-        if (a.vec_mode)
-            hipLaunchKernelGGL((k_fwd_csr<L, CPL, true, V>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
-                               a.senders, a.out);
-        else
-            hipLaunchKernelGGL((k_fwd_csr<L, CPL, false, V>), grid, block, 0, st, a.C, a.x, a.y, a.w, a.row_ptr,
-                               a.senders, a.out);
+        const bool split = CPL == 1 && V == kVariantSummed && (long)a.n_nodes * m.tiles * m.waves < kSplitBelowWaves;
+        if constexpr (CPL == 1 && V == kVariantSummed)
+            if (split) return fwd_csr_launch<L, CPL, V, true>(a, m, st);
+        return fwd_csr_launch<L, CPL, V, false>(a, m, st);
     } else {
         const long n = (long)a.n_nodes * Spec<L, L, L, V>::DO * a.C;
         hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, st, a.out, n);
@@ -660,17 +710,28 @@ hipError_t fwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int L, int CPL, int V, bool SPLIT>
+hipError_t bwd_launch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
+    const dim3 grid(a.n_nodes, SPLIT ? 2 : 1), block(64 * m.waves);
+    if (SPLIT) {
+        const long n = (long)a.n_nodes * Spec<L, L, L, V>::D1 * a.C;
+        hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, st, a.dx, n);
+    }
+    if (a.vec_mode)
+        hipLaunchKernelGGL((k_bwd_sender<L, CPL, true, V, SPLIT>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+                           a.send_ptr, a.send_perm, a.send_recv, a.dx, a.dw, a.dy);
+    else
+        hipLaunchKernelGGL((k_bwd_sender<L, CPL, false, V, SPLIT>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+                           a.send_ptr, a.send_perm, a.send_recv, a.dx, a.dw, a.dy);
+    return hipGetLastError();
+}
+
 template <int L, int CPL, int V>
 hipError_t bwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
     static_assert(CPL == 1, "the backward maps one channel per lane");
-    dim3 grid(a.n_nodes), block(64 * m.waves);
-    if (a.vec_mode)
-        hipLaunchKernelGGL((k_bwd_sender<L, CPL, true, V>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
-                           a.send_ptr, a.send_perm, a.send_recv, a.dx, a.dw, a.dy);
-    else
-        hipLaunchKernelGGL((k_bwd_sender<L, CPL, false, V>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
-                           a.send_ptr, a.send_perm, a.send_recv, a.dx, a.dw, a.dy);
-    return hipGetLastError();
+    if constexpr (V == kVariantSummed)
+        if ((long)a.n_nodes * m.waves < kSplitBelowWaves) return bwd_launch<L, CPL, V, true>(a, m, st);
+    return bwd_launch<L, CPL, V, false>(a, m, st);
 }
 
 template <int L>

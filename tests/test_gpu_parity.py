@@ -125,6 +125,16 @@ def test_two_channels_per_lane(ctp, dev, L, y_mode):
     run_small(ctp, dev, d, L, y_mode, 0, bwd=False)
 
 
+@pytest.mark.parametrize("n,c,L", [(4096, 64, 3), (2048, 128, 2)])
+@pytest.mark.parametrize("y_mode", [0, 1])
+def test_unsplit_rows(ctp, dev, n, c, L, y_mode):
+    # Grids of fewer than 4096 waves split every edge list between two
+    # workgroups (partial sums added with two fp32 atomics onto zero); these
+    # sizes are just large enough to take the unsplit path, element by element.
+    d = gen.poisson_small(n, c, L, mean_deg=3.0, seed=n + c)
+    run_small(ctp, dev, d, L, y_mode, 0, bwd=True)
+
+
 def test_deterministic_reruns(ctp, dev):
     d = gen.poisson_small(300, 128, 3, mean_deg=45.0, seed=5)
     g = ctp.Graph(300, T(d["row_ptr"], dev), T(d["senders"], dev))
