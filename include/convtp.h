@@ -56,9 +56,12 @@
  * indices are undefined behaviour; conv_tp_check_graph validates a graph.
  * On a non-zero status, conv_tp_last_error() returns a message (per thread).
  *
- * Determinism.  algo 0 (CSR forward) and the backward write each output
- * element once, summing in a fixed order: results are bitwise reproducible.
- * algo 1 (edge-parallel atomics) is not.
+ * Determinism.  algo 0 (CSR forward) and the backward sum in a fixed order
+ * and are bitwise reproducible.  On grids of fewer than 4096 waves each
+ * node's edge list is split between two workgroups whose two partial sums are
+ * added with fp32 atomics onto a zeroed output; two addends onto zero give
+ * the same result in either order, so this keeps the guarantee.  algo 1
+ * (edge-parallel atomics) is not reproducible.
  */
 #ifndef CONVTP_H
 #define CONVTP_H
