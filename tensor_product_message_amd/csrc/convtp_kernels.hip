@@ -390,6 +390,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
     __shared__ float sY[2][16];
     __shared__ float sRed[kBwdMaxThreads / 64][16];
     __shared__ SlotDev sTab[NT];
+    __shared__ ShCoef sSh[VEC ? 16 : 1];   // harmonic coefficients, read per edge from LDS
 
     const int j = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
@@ -417,6 +418,8 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
         {
             const SlotDev* tab = slot_tab<L, V>();
             for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
+            if constexpr (VEC)
+                if (tid < 16) sSh[tid] = sh_tab().k[tid];
         }
         float gv[D3][CPL], wv[P][CPL];
         long e = send_perm[k0];
@@ -542,7 +545,13 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
             // hold registers through the arithmetic above.
             const int tt = (int)opaque_lane((uint32_t)tid);
             const int ln = tt & 63;
-            const float ynext = sh_load<D2, VEC>(yv, e, tt);
+            float ynext;
+            if constexpr (VEC) {
+                const float* vp = yv + 3 * e;
+                ynext = tt < D2 ? sh_component_c(tt, sSh[tt < D2 ? tt : 0], vp[0], vp[1], vp[2]) : 0.0f;
+            } else {
+                ynext = sh_load<D2, VEC>(yv, e, tt);
+            }
             load_bwd_operands<S, CPL>(gv, wv, G, w, send_recv[kn], e, C, has_next ? voff : kOffLane);
             __builtin_amdgcn_sched_barrier(0);
 
@@ -567,7 +576,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
                     const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
                     float g[3] = {0.0f, 0.0f, 0.0f};
                     if (ln < D2) {
-                        sh_component_grad(ln, rx, ry, rz, g);
+                        sh_component_grad_c(sSh[ln], rx, ry, rz, g);
                         g[0] *= tot; g[1] *= tot; g[2] *= tot;
                     }
                     const float gx = lane_value(wave_sum_to_last(g[0]), 63);

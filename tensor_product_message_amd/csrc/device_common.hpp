@@ -165,21 +165,24 @@ __device__ __forceinline__ float horner4(const float* q, float z) {
     return ((q[3] * z + q[2]) * z + q[1]) * z + q[0];
 }
 
-// Y_k of the direction of v; |v| = 0 gives Y_0 = 1/sqrt(4pi) and 0 otherwise.
-__device__ __forceinline__ float sh_component(int k, float vx, float vy, float vz) {
+// Y_k of the direction of v with k's coefficients c; |v| = 0 gives
+// Y_0 = 1/sqrt(4pi) and 0 otherwise.
+__device__ __forceinline__ float sh_component_c(int k, const ShCoef& c, float vx, float vy, float vz) {
     const float n2 = vx * vx + vy * vy + vz * vz;
     if (n2 == 0.0f) return k == 0 ? 0.28209479177387814f : 0.0f;
     const float inv = 1.0f / sqrtf(n2);
     const float x = vx * inv, y = vy * inv, z = vz * inv;
-    const ShCoef& c = sh_tab().k[k];
     float re, im;
     xy_power(x, y, c.a, re, im);
     return (c.sine ? im : re) * horner4(c.q, z);
 }
 
+__device__ __forceinline__ float sh_component(int k, float vx, float vy, float vz) {
+    return sh_component_c(k, sh_tab().k[k], vx, vy, vz);
+}
+
 // dY_k / dr (gradient of the polynomial form at the unit vector r).
-__device__ __forceinline__ void sh_component_grad(int k, float x, float y, float z, float g[3]) {
-    const ShCoef& c = sh_tab().k[k];
+__device__ __forceinline__ void sh_component_grad_c(const ShCoef& c, float x, float y, float z, float g[3]) {
     const float Q = horner4(c.q, z), dQ = horner4(c.dq, z);
     const int a = c.a;
     const float fa = static_cast<float>(a);
@@ -199,6 +202,10 @@ __device__ __forceinline__ void sh_component_grad(int k, float x, float y, float
     g[0] = dAx * Q;
     g[1] = dAy * Q;
     g[2] = A * dQ;
+}
+
+__device__ __forceinline__ void sh_component_grad(int k, float x, float y, float z, float g[3]) {
+    sh_component_grad_c(sh_tab().k[k], x, y, z, g);
 }
 
 // ------------------------------------------------------------ wavefront reductions (wave64, DPP)
