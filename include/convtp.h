@@ -147,7 +147,8 @@ int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const fl
  *   Y -> a_y; g_y = dY with x -> a_x plus w -> a_w.
  * Layouts and graph arrays as for conv_tp_bwd (a_x like x, a_w like w, a_y
  * like Y).  y_mode must be 0 and algo 0 (CTP_EUNSUPPORTED otherwise); C <= 512.
- * Every output is written once in a fixed order (bitwise reproducible). */
+ * Every output is written once in a fixed order (bitwise reproducible).  For
+ * edge vectors see conv_tp_sh_jvp / conv_tp_sh_bwd_bwd below. */
 int32_t conv_tp_bwd_bwd(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y,
                         const float *w, const float *a_x, const float *a_w, const float *a_y, const int32_t *row_ptr,
                         const int32_t *senders, const int32_t *send_ptr, const int32_t *send_perm,
@@ -159,6 +160,21 @@ int32_t conv_tp_sh(int32_t n_edges, int32_t l_sh, const float *vec, float *Y, vo
 /* Vector gradient of the harmonics: dvec[e] = (dY/dvec)(vec_e)^T dY[e]. */
 int32_t conv_tp_sh_bwd(int32_t n_edges, int32_t l_sh, const float *vec, const float *dY, float *dvec,
                        void *stream);
+
+/* Second-order terms of the harmonics, for the VJP of the backward with edge
+ * vectors (force training).  With Y = Y(vec), J = dY/dvec [E][D_sh][3]:
+ *   conv_tp_sh_jvp:     a_y[e] = J(vec_e) a_vec[e]                    ([E][D_sh])
+ *   conv_tp_sh_bwd_bwd: g_vec[e] = J^T g_y[e] + d/dvec <J a_vec[e], dY[e]>  ([E][3])
+ * With cotangents (a_x, a_w, a_vec) of the edge-vector backward's (dx, dw,
+ * dvec), its VJP is: a_y = conv_tp_sh_jvp(vec, a_vec); (g_x, g_w, g_y, g_grad)
+ * = conv_tp_bwd_bwd with Y = conv_tp_sh(vec) and that a_y; g_vec =
+ * conv_tp_sh_bwd_bwd(vec, dY, a_vec, g_y), where dY is the first backward's
+ * harmonic gradient (conv_tp_bwd with Y given).  A zero vector gives zeros.
+ * All arrays device, 4-byte aligned. */
+int32_t conv_tp_sh_jvp(int32_t n_edges, int32_t l_sh, const float *vec, const float *a_vec, float *a_y,
+                       void *stream);
+int32_t conv_tp_sh_bwd_bwd(int32_t n_edges, int32_t l_sh, const float *vec, const float *dY, const float *a_vec,
+                           const float *g_y, float *g_vec, void *stream);
 
 /* Sender-sorted transpose of a CSR-by-receiver graph: send_ptr[N+1],
  * send_perm[E] (CSR edge ids, ascending within each sender) and

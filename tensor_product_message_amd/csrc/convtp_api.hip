@@ -308,6 +308,32 @@ int32_t conv_tp_sh_bwd(int32_t n_edges, int32_t l_sh, const float* vec, const fl
                       "conv_tp_sh_bwd launch");
 }
 
+int32_t conv_tp_sh_jvp(int32_t n_edges, int32_t l_sh, const float* vec, const float* a_vec, float* a_y,
+                       void* stream) {
+    if (n_edges < 0) return fail(CTP_EINVAL, "negative edge count");
+    if (int r = check_degree(l_sh, "l_sh")) return r;
+    if (int r = need(vec, (int64_t)n_edges * 3, 4, "vec")) return r;
+    if (int r = need(a_vec, (int64_t)n_edges * 3, 4, "a_vec")) return r;
+    if (int r = need(a_y, (int64_t)n_edges * ctp::dim_of(l_sh), 4, "a_y")) return r;
+    return hip_status(ctp::launch_sh_jvp(l_sh, n_edges, vec, a_vec, a_y, static_cast<hipStream_t>(stream)),
+                      "conv_tp_sh_jvp launch");
+}
+
+int32_t conv_tp_sh_bwd_bwd(int32_t n_edges, int32_t l_sh, const float* vec, const float* dY, const float* a_vec,
+                           const float* g_y, float* g_vec, void* stream) {
+    if (n_edges < 0) return fail(CTP_EINVAL, "negative edge count");
+    if (int r = check_degree(l_sh, "l_sh")) return r;
+    const int64_t D = ctp::dim_of(l_sh);
+    if (int r = need(vec, (int64_t)n_edges * 3, 4, "vec")) return r;
+    if (int r = need(dY, (int64_t)n_edges * D, 4, "dY")) return r;
+    if (int r = need(a_vec, (int64_t)n_edges * 3, 4, "a_vec")) return r;
+    if (int r = need(g_y, (int64_t)n_edges * D, 4, "g_y")) return r;
+    if (int r = need(g_vec, (int64_t)n_edges * 3, 4, "g_vec")) return r;
+    return hip_status(ctp::launch_sh_bwd_bwd(l_sh, n_edges, vec, dY, a_vec, g_y, g_vec,
+                                             static_cast<hipStream_t>(stream)),
+                      "conv_tp_sh_bwd_bwd launch");
+}
+
 int32_t conv_tp_build_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* row_ptr, const int32_t* senders,
                                 int32_t* send_ptr, int32_t* send_perm, int32_t* send_recv, void* stream) {
     if (n_nodes < 0 || n_edges < 0) return fail(CTP_EINVAL, "negative node or edge count");

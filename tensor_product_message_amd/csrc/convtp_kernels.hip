@@ -653,6 +653,90 @@ __global__ void k_sh_bwd(long n_edges, const float* __restrict__ vec, const floa
     dvec[3 * e + 2] = (gz - rg * rz) * inv;
 }
 
+// Second-order terms for edge vectors (the VJP of the backward when the
+// harmonics are evaluated from vec; r = v/|v|, n = |v|, P = I - r r^T):
+//   aY[e, k] = (J a)_k = g_k . P a / n                       (k_sh_jvp)
+//   gvec[e]  = J^T gY + d/dv < J a, dY >                     (k_sh_bwd_bwd)
+// with g_k, H_k the gradient and Hessian of Y_k's polynomial form in r.  For
+// u = sum dY_k g_k, M = sum dY_k H_k and f = u . P a:
+//   d/dv < J a, dY > = (P grad_r f - f r) / n^2,
+//   grad_r f = M a - (r . a)(M r + u) - (u . r) a.
+template <int L>
+__global__ void k_sh_jvp(long n_edges, const float* __restrict__ vec, const float* __restrict__ a,
+                         float* __restrict__ aY) {
+    constexpr int D = (L + 1) * (L + 1);
+    const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_edges * D) return;
+    const long e = t / D;
+    const int k = static_cast<int>(t - e * D);
+    const float vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    const float n2 = vx * vx + vy * vy + vz * vz;
+    if (n2 == 0.0f) {
+        aY[t] = 0.0f;
+        return;
+    }
+    const float inv = 1.0f / sqrtf(n2);
+    const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
+    const float ax = a[3 * e], ay = a[3 * e + 1], az = a[3 * e + 2];
+    float g[3];
+    sh_component_grad(k, rx, ry, rz, g);
+    const float ga = g[0] * ax + g[1] * ay + g[2] * az;
+    const float gr = g[0] * rx + g[1] * ry + g[2] * rz;
+    const float ra = rx * ax + ry * ay + rz * az;
+    aY[t] = (ga - gr * ra) * inv;
+}
+
+template <int L>
+__global__ void k_sh_bwd_bwd(long n_edges, const float* __restrict__ vec, const float* __restrict__ dY,
+                             const float* __restrict__ a, const float* __restrict__ gY, float* __restrict__ gvec) {
+    constexpr int D = (L + 1) * (L + 1);
+    const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n_edges) return;
+    const float vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    const float n2 = vx * vx + vy * vy + vz * vz;
+    if (n2 == 0.0f) {
+        gvec[3 * e] = gvec[3 * e + 1] = gvec[3 * e + 2] = 0.0f;
+        return;
+    }
+    const float inv = 1.0f / sqrtf(n2);
+    const float r[3] = {vx * inv, vy * inv, vz * inv};
+    const float av[3] = {a[3 * e], a[3 * e + 1], a[3 * e + 2]};
+    float wv[3] = {0.0f, 0.0f, 0.0f}, u[3] = {0.0f, 0.0f, 0.0f};
+    float M[6] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};   // xx, xy, yy, xz, yz, zz
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        float g[3], h[6];
+        sh_component_hess(k, r[0], r[1], r[2], g, h);
+        const float gy = gY[e * D + k], dy = dY[e * D + k];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            wv[i] = __builtin_fmaf(gy, g[i], wv[i]);
+            u[i] = __builtin_fmaf(dy, g[i], u[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i) M[i] = __builtin_fmaf(dy, h[i], M[i]);
+    }
+    auto mul = [&](const float* q, float* o) {
+        o[0] = M[0] * q[0] + M[1] * q[1] + M[3] * q[2];
+        o[1] = M[1] * q[0] + M[2] * q[1] + M[4] * q[2];
+        o[2] = M[3] * q[0] + M[4] * q[1] + M[5] * q[2];
+    };
+    const float wr = wv[0] * r[0] + wv[1] * r[1] + wv[2] * r[2];
+    const float ur = u[0] * r[0] + u[1] * r[1] + u[2] * r[2];
+    const float ra = r[0] * av[0] + r[1] * av[1] + r[2] * av[2];
+    const float f = (u[0] * av[0] + u[1] * av[1] + u[2] * av[2]) - ur * ra;
+    float Ma[3], Mr[3], df[3];
+    mul(av, Ma);
+    mul(r, Mr);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) df[i] = Ma[i] - ra * (Mr[i] + u[i]) - ur * av[i];
+    const float dfr = df[0] * r[0] + df[1] * r[1] + df[2] * r[2];
+    const float inv2 = inv * inv;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        gvec[3 * e + i] = (wv[i] - wr * r[i]) * inv + (df[i] - dfr * r[i] - f * r[i]) * inv2;
+}
+
 // ------------------------------------------------------------ launchers
 
 namespace {
@@ -821,6 +905,34 @@ hipError_t launch_sh_bwd(int L, long n_edges, const float* vec, const float* dY,
         case 1: hipLaunchKernelGGL(k_sh_bwd<1>, grid, block, 0, st, n_edges, vec, dY, dvec); break;
         case 2: hipLaunchKernelGGL(k_sh_bwd<2>, grid, block, 0, st, n_edges, vec, dY, dvec); break;
         case 3: hipLaunchKernelGGL(k_sh_bwd<3>, grid, block, 0, st, n_edges, vec, dY, dvec); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sh_jvp(int L, long n_edges, const float* vec, const float* a, float* aY, hipStream_t st) {
+    if (n_edges == 0) return hipSuccess;
+    const long n = n_edges * (L + 1) * (L + 1);
+    const dim3 block(256), grid((unsigned)((n + 255) / 256));
+    switch (L) {
+        case 0: hipLaunchKernelGGL(k_sh_jvp<0>, grid, block, 0, st, n_edges, vec, a, aY); break;
+        case 1: hipLaunchKernelGGL(k_sh_jvp<1>, grid, block, 0, st, n_edges, vec, a, aY); break;
+        case 2: hipLaunchKernelGGL(k_sh_jvp<2>, grid, block, 0, st, n_edges, vec, a, aY); break;
+        case 3: hipLaunchKernelGGL(k_sh_jvp<3>, grid, block, 0, st, n_edges, vec, a, aY); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sh_bwd_bwd(int L, long n_edges, const float* vec, const float* dY, const float* a, const float* gY,
+                             float* gvec, hipStream_t st) {
+    if (n_edges == 0) return hipSuccess;
+    const dim3 block(256), grid((unsigned)((n_edges + 255) / 256));
+    switch (L) {
+        case 0: hipLaunchKernelGGL(k_sh_bwd_bwd<0>, grid, block, 0, st, n_edges, vec, dY, a, gY, gvec); break;
+        case 1: hipLaunchKernelGGL(k_sh_bwd_bwd<1>, grid, block, 0, st, n_edges, vec, dY, a, gY, gvec); break;
+        case 2: hipLaunchKernelGGL(k_sh_bwd_bwd<2>, grid, block, 0, st, n_edges, vec, dY, a, gY, gvec); break;
+        case 3: hipLaunchKernelGGL(k_sh_bwd_bwd<3>, grid, block, 0, st, n_edges, vec, dY, a, gY, gvec); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -208,6 +208,45 @@ __device__ __forceinline__ void sh_component_grad(int k, float x, float y, float
     sh_component_grad_c(sh_tab().k[k], x, y, z, g);
 }
 
+// Gradient g and Hessian h = (xx, xy, yy, xz, yz, zz) in r of the polynomial
+// form of Y_k (r a free vector).  With w = x + iy and A = Re w^a (Im w^a):
+// A_x = a Re w^(a-1) (a Im), A_y = -a Im w^(a-1) (a Re), A_xx = a(a-1) Re w^(a-2)
+// (a(a-1) Im), A_xy = -a(a-1) Im w^(a-2) (a(a-1) Re), A_yy = -A_xx.
+__device__ __forceinline__ void sh_component_hess(int k, float x, float y, float z, float g[3], float h[6]) {
+    const ShCoef& c = sh_tab().k[k];
+    const float Q = horner4(c.q, z), dQ = horner4(c.dq, z);
+    const float d2Q = c.dq[1] + 2.0f * c.dq[2] * z + 3.0f * c.dq[3] * z * z;
+    const int a = c.a;
+    const float fa = static_cast<float>(a), fb = static_cast<float>(a * (a - 1));
+    float re, im, r1, i1, r2, i2;
+    xy_power(x, y, a, re, im);
+    xy_power(x, y, a > 0 ? a - 1 : 0, r1, i1);
+    xy_power(x, y, a > 1 ? a - 2 : 0, r2, i2);
+    float A, Ax, Ay, Axx, Axy;
+    if (c.sine) {
+        A = im;
+        Ax = fa * i1;
+        Ay = fa * r1;
+        Axx = fb * i2;
+        Axy = fb * r2;
+    } else {
+        A = re;
+        Ax = fa * r1;
+        Ay = -fa * i1;
+        Axx = fb * r2;
+        Axy = -fb * i2;
+    }
+    g[0] = Ax * Q;
+    g[1] = Ay * Q;
+    g[2] = A * dQ;
+    h[0] = Axx * Q;
+    h[1] = Axy * Q;
+    h[2] = -Axx * Q;
+    h[3] = Ax * dQ;
+    h[4] = Ay * dQ;
+    h[5] = A * d2Q;
+}
+
 // ------------------------------------------------------------ wavefront reductions (wave64, DPP)
 
 template <int Ctrl, int RowMask = 0xf>

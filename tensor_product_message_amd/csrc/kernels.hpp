@@ -50,6 +50,9 @@ hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st);
 bool bwd_supports_channels(int C);
 hipError_t launch_sh(int L, long n_edges, const float* vec, float* Y, hipStream_t st);
 hipError_t launch_sh_bwd(int L, long n_edges, const float* vec, const float* dY, float* dvec, hipStream_t st);
+hipError_t launch_sh_jvp(int L, long n_edges, const float* vec, const float* a, float* aY, hipStream_t st);
+hipError_t launch_sh_bwd_bwd(int L, long n_edges, const float* vec, const float* dY, const float* a, const float* gY,
+                             float* gvec, hipStream_t st);
 
 hipError_t launch_transpose(int n_nodes, int n_edges, const int32_t* row_ptr, const int32_t* senders,
                             int32_t* send_ptr, int32_t* send_perm, int32_t* send_recv, hipStream_t st);

@@ -279,6 +279,42 @@ def stream_probe(kind: int, src, dst):
     check(lib().conv_tp_stream_probe(kind, _p(src), _p(dst), n, _stream(t)))
 
 
+def spherical_harmonics_jvp(vec, a_vec, lmax: int, out=None):
+    """a_Y = (dY/dvec) a_vec per edge."""
+    e = vec.shape[0]
+    _want(vec, "vec", (e, 3))
+    _want(a_vec, "a_vec", (e, 3), device=vec.device)
+    out = torch.empty((e, dim(lmax)), dtype=torch.float32, device=vec.device) if out is None else out
+    _want(out, "a_y", (e, dim(lmax)), device=vec.device)
+    check(lib().conv_tp_sh_jvp(e, lmax, _p(vec), _p(a_vec), _p(out), _stream(vec)))
+    return out
+
+
+def spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, lmax: int, out=None):
+    """g_vec = J^T g_y + d/dvec <J a_vec, dY> per edge."""
+    e = vec.shape[0]
+    _want(vec, "vec", (e, 3))
+    for name, t, sh_ in (("dY", dY, (e, dim(lmax))), ("a_vec", a_vec, (e, 3)), ("g_y", g_y, (e, dim(lmax)))):
+        _want(t, name, sh_, device=vec.device)
+    out = torch.empty_like(vec) if out is None else out
+    _want(out, "g_vec", (e, 3), device=vec.device)
+    check(lib().conv_tp_sh_bwd_bwd(e, lmax, _p(vec), _p(dY), _p(a_vec), _p(g_y), _p(out), _stream(vec)))
+    return out
+
+
+def conv_tp_bwd_bwd_vec(grad_out, x, vec, w, a_x, a_w, a_vec, graph: Graph, lmax: int):
+    """VJP of the edge-vector backward: (g_x, g_w, g_vec, g_grad) for
+    cotangents (a_x, a_w, a_vec) of (dx, dw, dvec), by the library calls
+    include/convtp.h lists (harmonics, first backward with Y given for dY,
+    harmonic JVP, the double backward, and the harmonic second-order term)."""
+    Y = spherical_harmonics(vec, lmax)
+    _, _, dY = conv_tp_bwd(grad_out, x, Y, w, graph, lmax, Y_GIVEN)
+    a_y = spherical_harmonics_jvp(vec, a_vec, lmax)
+    g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph, lmax)
+    g_vec = spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, lmax)
+    return g_x, g_w, g_vec, g_grad
+
+
 class ConvTPFunction(torch.autograd.Function):
     """Autograd wrapper: forward = conv_tp_fwd (algo 0), backward = conv_tp_bwd."""
 

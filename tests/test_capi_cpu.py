@@ -195,6 +195,14 @@ def test_other_entry_points_validate(capi):
     assert L.conv_tp_sh(5, 4, A, A, NUL) == capi.CTP_EUNSUPPORTED
     assert L.conv_tp_sh(5, 2, NUL, A, NUL) == capi.CTP_EINVAL
     assert L.conv_tp_sh_bwd(5, 2, A, A, NUL, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_sh_jvp(5, 2, A, NUL, A2, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_sh_jvp(5, 4, A, A, A2, NUL) == capi.CTP_EUNSUPPORTED
+    assert L.conv_tp_sh_jvp(-5, 2, A, A, A2, NUL) == capi.CTP_EINVAL
+    for k in range(5):
+        a = [A, A, A, A, A2]
+        a[k] = NUL
+        assert L.conv_tp_sh_bwd_bwd(5, 2, *a, NUL) == capi.CTP_EINVAL, k
+    assert L.conv_tp_sh_bwd_bwd(0, 3, NUL, NUL, NUL, NUL, NUL, NUL) == capi.CTP_OK
     assert L.conv_tp_build_transpose(-1, 0, A, A, A, A, A, NUL) == capi.CTP_EINVAL
     assert L.conv_tp_build_transpose(0, 3, A, A, A, A, A, NUL) == capi.CTP_EGRAPH
     assert L.conv_tp_build_transpose(4, 3, A, A, NUL, A, A, NUL) == capi.CTP_EINVAL

@@ -496,3 +496,47 @@ def test_variant_slots_full_l3_sampled(ctp, dev):
     ei = torch.as_tensor(edges, device=dev)
     close("dw[sample]", host(dw[ei]), dw_ref)
     close("dY[sample]", host(dy[ei]), dY_ref)
+
+
+# ------------------------------------------------------------ edge-vector VJP of the VJP
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3])
+def test_harmonic_second_order_terms(ctp, dev, L):
+    rng = np.random.default_rng(60 + L)
+    e = 5000
+    vec = rng.standard_normal((e, 3)).astype(np.float32) * rng.uniform(0.3, 3.0, (e, 1)).astype(np.float32)
+    vec[0] = 0.0                      # zero vector: zeros by convention
+    vec[1] = [0.0, 0.0, 2.0]          # poles
+    vec[2] = [0.0, 0.0, -0.5]
+    av = rng.standard_normal((e, 3)).astype(np.float32)
+    dY = rng.standard_normal((e, (L + 1) ** 2)).astype(np.float32)
+    gY = rng.standard_normal((e, (L + 1) ** 2)).astype(np.float32)
+    v64 = vec.astype(np.float64)
+    aY = ctp.spherical_harmonics_jvp(T(vec, dev), T(av, dev), L)
+    gv = ctp.spherical_harmonics_bwd_bwd(T(vec, dev), T(dY, dev), T(av, dev), T(gY, dev), L)
+    ref_aY = osh.real_sh_jvp(L, v64, av)
+    ref_gv = osh.vec_grad_from_sh_grad(L, v64, gY) + osh.vec_hess_term(L, v64, dY, av)
+    close("aY", host(aY), ref_aY, nonzero=L > 0)
+    close("gvec", host(gv), ref_gv, nonzero=L > 0)
+    assert np.all(host(aY)[0] == 0.0) and np.all(host(gv)[0] == 0.0)
+
+
+@pytest.mark.parametrize("n,c,L", [(60, 16, 1), (80, 64, 2), (70, 128, 3)])
+def test_double_bwd_edge_vectors(ctp, dev, n, c, L):
+    d = gen.poisson_small(n, c, L, mean_deg=10.0, seed=n + L)
+    prob = oc.Problem(L, L, L)
+    ax, aw, _ = gen.cotangents_small(d, seed=n)
+    av = np.random.default_rng(n + 1).standard_normal((d["n_edges"], 3)).astype(np.float32)
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    gx, gw, gvec, gG = ctp.conv_tp_bwd_bwd_vec(T(d["grad_out"], dev), T(d["x"], dev), T(d["vec"], dev),
+                                               T(d["w"], dev), T(ax, dev), T(aw, dev), T(av, dev), g, L)
+    v64 = d["vec"].astype(np.float64)
+    Y = osh.real_sh(L, v64)
+    aY = osh.real_sh_jvp(L, v64, av)
+    rx, rw, rY, rG = oc.materialised_double_bwd(prob, d["x"], Y, d["w"], d["grad_out"], ax, aw, aY,
+                                                d["row_ptr"], d["senders"])
+    _, _, dY = oc.materialised_bwd(prob, d["x"], Y, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+    rvec = osh.vec_grad_from_sh_grad(L, v64, rY) + osh.vec_hess_term(L, v64, dY, av)
+    for name, got, ref in (("g_x", gx, rx), ("g_w", gw, rw), ("g_vec", gvec, rvec), ("g_grad", gG, rG)):
+        close(name, host(got), ref)
