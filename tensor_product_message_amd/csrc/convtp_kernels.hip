@@ -233,6 +233,7 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
     __shared__ __attribute__((aligned(16))) float sT[2][NTP];
     __shared__ float sY[2][16];
     __shared__ SlotDev sTab[NT];
+    __shared__ ShCoef sSh[VEC ? 16 : 1];   // harmonic coefficients, read per edge from LDS
 
     const int i = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
@@ -255,6 +256,8 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
         {
             const SlotDev* tab = slot_tab<L, V>();
             for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
+            if constexpr (VEC)
+                if (tid < 16) sSh[tid] = sh_tab().k[tid];
         }
         float xv[D1][CPL], wv[P][CPL];
         load_edge_operands<S, CPL>(xv, wv, x, w, senders[e0], e0, C, voff);
@@ -271,7 +274,13 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
             const rsrc_t nx = make_row(x + jn * D1 * C, (long)D1 * C);
             const rsrc_t nw = make_row(w + en * P * C, (long)P * C);
             const uint32_t nvoff = has_next ? voff : kOffLane;
-            const float ynext = sh_value<D2, VEC>(yv, en, tid);
+            float ynext;
+            if constexpr (VEC) {
+                const float* vp = yv + 3 * en;
+                ynext = tid < D2 ? sh_component_c(tid, sSh[tid < D2 ? tid : 0], vp[0], vp[1], vp[2]) : 0.0f;
+            } else {
+                ynext = sh_value<D2, VEC>(yv, en, tid);
+            }
             edge_forward_refill<S, CPL>(acc, xv, wv, sT[buf], nx, nw, nvoff, C);
             if (has_next) {
                 if (tid < D2) sY[buf ^ 1][tid] = ynext;
