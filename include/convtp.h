@@ -4,9 +4,9 @@
  *
  * The operation is the message-passing convolution of MACE-style interatomic
  * potentials that the e3j paper (arXiv 2609.35099) accelerates: abstract
- * ("message passing convolutions forward"), Table 1 (convolution throughput
- * by channel count) and Table 2 (only the convolution block of MACE runs on
- * the dedicated kernels).  For every edge e = j -> i:
+ * (the forward of message-passing convolutions), Table 1 (convolution
+ * throughput by channel count) and Table 2 (only the convolution block of
+ * MACE runs on the dedicated kernels).  For every edge e = j -> i:
  *
  *   out[i, l3 m3, c] = sum_e sum_{p = (l1,l2,l3)} w[e, p, c]
  *                      sum_{m1,m2} C_p[m1][m2][m3] x[j, l1 m1, c] Y[e, l2 m2]

@@ -13,16 +13,20 @@
 // edges in CSR-by-receiver order.
 //
 // Mapping: one workgroup per receiver (forward) or sender (backward) and per
-// channel tile; lane <-> channel (CPL = 1 or 2 adjacent channels per lane).
-// Per edge, T_{p,e} is shared by every channel: the workgroup builds it once
-// in LDS (lane-parallel, <= 2 terms per entry) and every lane then reads it by
-// broadcast.  The path loops are unrolled at compile time over the constexpr
-// tables, so each coupling coefficient is an instruction constant and every
-// partial sum lives in registers.
+// channel tile; a lane owns channels c0 + 64 c, c < CPL (CPL = 1 or 2), so
+// every wave-wide access covers 256 contiguous bytes.  Per edge, T_{p,e} is
+// shared by every channel: the workgroup builds it once in LDS (lane-parallel,
+// <= 2 terms per entry) and every lane then reads it by broadcast.  The path
+// loops are unrolled at compile time over the constexpr tables, so each
+// coupling coefficient is an instruction constant and every partial sum lives
+// in registers.  The path variant V (all paths summed per l3, or MACE's
+// natural-parity paths with one output slot each) is a template parameter.
 //
-// Determinism: the CSR forward and the sender-sorted backward write every
-// output element exactly once, summing edges and paths in a fixed order (no
-// atomics).  The edge-parallel atomic forward exists only as a comparison.
+// Determinism: the CSR forward and the sender-sorted backward sum edges and
+// paths in a fixed order.  Small grids (SPLIT) divide each edge list between
+// two workgroups whose two partial sums meet by fp32 atomics onto zero, which
+// gives the same bits in either order.  The edge-parallel atomic forward
+// exists only as a comparison.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
