@@ -137,6 +137,31 @@ int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const fl
                     const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec,
                     void *stream);
 
+/* Bytes of device workspace conv_tp_bwd_msg needs: E * D_in * C * 4 with
+ * D_in = (l_in+1)^2.  Pure host function; errors as conv_tp_bwd's problem
+ * checks, CTP_EINVAL for a null bytes pointer. */
+int32_t conv_tp_bwd_msg_workspace(const conv_tp_problem *prob, int64_t *bytes);
+
+/* The same backward (same arguments, outputs and math as conv_tp_bwd, e3j's
+ * backward section) in two passes through a caller-owned device workspace
+ * msg[E][D_in][C] (CSR edge order, 16-byte aligned, at least
+ * conv_tp_bwd_msg_workspace bytes, else CTP_EINVAL; contents on entry are
+ * ignored and overwritten).  Pass 1, one workgroup per receiver i: G[i] is
+ * read once, and for each in-edge e = j -> i in CSR order the kernel stores
+ * dw[e], dY[e] (or dvec[e]) and the edge's message
+ * msg[e] = sum_p w[e,p] (T_p(Y_e)^T G[i])_p, the edge's share of dx[j].
+ * Pass 2: dx[j] = sum over j's out-edges in (send_ptr, send_perm) order of
+ * msg[e].  For variant 1 the G row is much wider than x's (99 against 16
+ * components at l = 3), so reading G once per receiver instead of once per
+ * edge moves fewer bytes; for variant 0 conv_tp_bwd moves fewer.  dw and dY
+ * are bitwise those of conv_tp_bwd; dx differs only in the order of its fp32
+ * additions (per edge, then over edges) and is reproducible.  algo 0; C <= 512.
+ * Calls that share a workspace must not overlap. */
+int32_t conv_tp_bwd_msg(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y_or_vec,
+                        const float *w, const int32_t *row_ptr, const int32_t *senders, const int32_t *send_ptr,
+                        const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw,
+                        float *dy_or_dvec, float *workspace, int64_t workspace_bytes, void *stream);
+
 /* VJP of the backward (the "VJP-of-VJP" of FlashCart's section on symbolic
  * VJPs, needed to train on forces), Y given.  With cotangents a_x, a_w, a_y of
  * conv_tp_bwd's outputs (dx, dw, dY) and L2 = <a_x, dx> + <a_w, dw> + <a_y, dY>,
@@ -236,7 +261,8 @@ int32_t conv_tp_stream_probe(int32_t kind, const float *src, float *dst, int64_t
 /* Message for the last non-zero status on this thread ("" if none). */
 const char *conv_tp_last_error(void);
 
-/* ABI version (major * 100 + minor): 101 added conv_tp_problem.variant. */
+/* ABI version (major * 100 + minor): 101 added conv_tp_problem.variant, 102
+ * conv_tp_bwd_msg. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

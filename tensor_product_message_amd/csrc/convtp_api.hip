@@ -99,6 +99,47 @@ ctp::LaunchArgs base_args(const conv_tp_problem* pr) {
     return a;
 }
 
+// Checks shared by the two backward entry points; fills the launch arguments.
+int bwd_args(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* y_or_vec,
+             const float* w, const int32_t* row_ptr, const int32_t* senders, const int32_t* send_ptr,
+             const int32_t* send_perm, const int32_t* send_recv, float* dx, float* dw, float* dy_or_dvec, Shape* sp,
+             ctp::LaunchArgs* out) {
+    Shape& s = *sp;
+    if (int r = check_problem(prob, &s)) return r;
+    if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the backward has only the deterministic algorithm (algo 0)");
+    if (!ctp::bwd_supports_channels(prob->channels))
+        return fail(CTP_EUNSUPPORTED, "backward needs C <= 512, got %d", prob->channels);
+    if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
+    if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
+    if (int r = need(y_or_vec, s.E * s.S, 4, "y_or_vec")) return r;
+    if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;
+    if (int r = need(row_ptr, s.N + 1, 4, "row_ptr")) return r;
+    if (int r = need(senders, s.E, 4, "senders")) return r;
+    if (int r = need(send_ptr, s.N + 1, 4, "send_ptr")) return r;
+    if (int r = need(send_perm, s.E, 4, "send_perm")) return r;
+    if (int r = need(send_recv, s.E, 4, "send_recv")) return r;
+    if (int r = need(dx, s.N * s.D1 * s.C, 16, "dx")) return r;
+    if (int r = need(dw, s.E * s.P * s.C, 16, "dw")) return r;
+    if (int r = need(dy_or_dvec, s.E * s.S, 4, "dy_or_dvec")) return r;
+    ctp::LaunchArgs a = base_args(prob);
+    a.grad = grad_out;
+    a.x = x;
+    a.y = y_or_vec;
+    a.w = w;
+    a.row_ptr = row_ptr;
+    a.senders = senders;
+    a.send_ptr = send_ptr;
+    a.send_perm = send_perm;
+    a.send_recv = send_recv;
+    a.dx = dx;
+    a.dw = dw;
+    a.dy = dy_or_dvec;
+    *out = a;
+    return CTP_OK;
+}
+
+int64_t msg_workspace_bytes(const Shape& s) { return s.E * s.D1 * s.C * (int64_t)sizeof(float); }
+
 std::mutex g_bad_mu;
 std::unordered_map<int, unsigned long long*> g_bad_buf;   // per-device counter for conv_tp_check_graph
 
@@ -137,7 +178,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 101; }
+int32_t conv_tp_version(void) { return 102; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
@@ -200,41 +241,42 @@ int32_t conv_tp_fwd(const conv_tp_problem* prob, const float* x, const float* y_
     return hip_status(ctp::launch_fwd(a, static_cast<hipStream_t>(stream)), "conv_tp_fwd launch");
 }
 
+
 int32_t conv_tp_bwd(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* y_or_vec,
                     const float* w, const int32_t* row_ptr, const int32_t* senders, const int32_t* send_ptr,
                     const int32_t* send_perm, const int32_t* send_recv, float* dx, float* dw, float* dy_or_dvec,
                     void* stream) {
     Shape s{};
-    if (int r = check_problem(prob, &s)) return r;
-    if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the backward has only the deterministic algorithm (algo 0)");
-    if (!ctp::bwd_supports_channels(prob->channels))
-        return fail(CTP_EUNSUPPORTED, "backward needs C <= 512, got %d", prob->channels);
-    if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
-    if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
-    if (int r = need(y_or_vec, s.E * s.S, 4, "y_or_vec")) return r;
-    if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;
-    if (int r = need(row_ptr, s.N + 1, 4, "row_ptr")) return r;
-    if (int r = need(senders, s.E, 4, "senders")) return r;
-    if (int r = need(send_ptr, s.N + 1, 4, "send_ptr")) return r;
-    if (int r = need(send_perm, s.E, 4, "send_perm")) return r;
-    if (int r = need(send_recv, s.E, 4, "send_recv")) return r;
-    if (int r = need(dx, s.N * s.D1 * s.C, 16, "dx")) return r;
-    if (int r = need(dw, s.E * s.P * s.C, 16, "dw")) return r;
-    if (int r = need(dy_or_dvec, s.E * s.S, 4, "dy_or_dvec")) return r;
-    ctp::LaunchArgs a = base_args(prob);
-    a.grad = grad_out;
-    a.x = x;
-    a.y = y_or_vec;
-    a.w = w;
-    a.row_ptr = row_ptr;
-    a.senders = senders;
-    a.send_ptr = send_ptr;
-    a.send_perm = send_perm;
-    a.send_recv = send_recv;
-    a.dx = dx;
-    a.dw = dw;
-    a.dy = dy_or_dvec;
+    ctp::LaunchArgs a{};
+    if (int r = bwd_args(prob, grad_out, x, y_or_vec, w, row_ptr, senders, send_ptr, send_perm, send_recv, dx, dw,
+                         dy_or_dvec, &s, &a))
+        return r;
     return hip_status(ctp::launch_bwd(a, static_cast<hipStream_t>(stream)), "conv_tp_bwd launch");
+}
+
+int32_t conv_tp_bwd_msg_workspace(const conv_tp_problem* prob, int64_t* bytes) {
+    Shape s{};
+    if (int r = check_problem(prob, &s)) return r;
+    if (bytes == nullptr) return fail(CTP_EINVAL, "bytes is null");
+    *bytes = msg_workspace_bytes(s);
+    return ok();
+}
+
+int32_t conv_tp_bwd_msg(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* y_or_vec,
+                        const float* w, const int32_t* row_ptr, const int32_t* senders, const int32_t* send_ptr,
+                        const int32_t* send_perm, const int32_t* send_recv, float* dx, float* dw, float* dy_or_dvec,
+                        float* workspace, int64_t workspace_bytes, void* stream) {
+    Shape s{};
+    ctp::LaunchArgs a{};
+    if (int r = bwd_args(prob, grad_out, x, y_or_vec, w, row_ptr, senders, send_ptr, send_perm, send_recv, dx, dw,
+                         dy_or_dvec, &s, &a))
+        return r;
+    const int64_t need_bytes = msg_workspace_bytes(s);
+    if (workspace_bytes < need_bytes)
+        return fail(CTP_EINVAL, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)need_bytes);
+    if (int r = need(workspace, s.E * s.D1 * s.C, 16, "workspace")) return r;
+    return hip_status(ctp::launch_bwd_msg(a, workspace, static_cast<hipStream_t>(stream)), "conv_tp_bwd_msg launch");
 }
 
 int32_t conv_tp_bwd_bwd(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* y,

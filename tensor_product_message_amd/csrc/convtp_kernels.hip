@@ -386,6 +386,165 @@ __device__ __forceinline__ void load_bwd_operands(float (&gv)[S::DO][CPL], float
     for (int p = 0; p < S::P; ++p) bload<CPL, kStream>(wr, voff, (uint32_t)p * c4, wv[p]);
 }
 
+// One edge of the backward, given T = T(Y_e) in LDS, the sender's row x, the
+// receiver's row g of G and the edge's row w (one channel set per lane):
+//   v_p = T_p^T g,  dw[e,p] = x . v_p (stored through dwr),  dxa += w_p v_p,
+//   dya[l2 m2] += sum_p w_p B_p[m2],  B_p[m2] = sum C_p[m1][m2][m3] x[m1] g[m3].
+// Work is grouped by the paths that read one block of G: for each group, v_p,
+// dw_p and dx for its paths, then B_p from the products x[l1 m1] g[l3 m3]
+// formed m1 by m1 and shared by the group's paths.  A scheduling barrier after
+// each group bounds register lifetimes.  k_bwd_sender keeps an inline copy of
+// this loop: through the call the compiler's schedule for it needs 134 VGPRs
+// at L=3 instead of 122, one wave fewer per SIMD.
+template <int L, class S, int CPL>
+__device__ __forceinline__ void edge_backward(const float* T, const float (&xv)[S::D1][CPL],
+                                              const float (&gv)[S::DO][CPL], const float (&wv)[S::P][CPL],
+                                              rsrc_t dwr, uint32_t voff, int C, float (&dxa)[S::D1][CPL],
+                                              float (&dya)[16]) {
+    static_for<S::NG>([&](auto gI) __attribute__((always_inline)) {
+        constexpr PathGroup pp = S::groups[decltype(gI)::value];
+        constexpr int l1 = pp.l1, l3 = pp.l3;
+        constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
+        constexpr int o1 = l1 * l1, o3 = pp.o3;   // o3: the group's block of G
+        // (a) v_p = T_p^T g, dw_p = x . v_p, dx += w_p v_p
+        static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+            constexpr int p = pp.p[decltype(kI)::value];
+            constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
+            float v[n1][CPL];
+            static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
+                constexpr int t = t0 + decltype(tI)::value;
+                constexpr TSlot s = S::slots[t];
+                const float tv = slot_value<t>(T);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    if constexpr (first_m1<S>(t))
+                        v[s.m1][c] = tv * gv[o3 + s.m3][c];
+                    else
+                        v[s.m1][c] = __builtin_fmaf(tv, gv[o3 + s.m3][c], v[s.m1][c]);
+                }
+            });
+            float dwv[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                dwv[c] = xv[o1][c] * v[0][c];
+#pragma unroll
+                for (int a = 1; a < n1; ++a) dwv[c] = __builtin_fmaf(xv[o1 + a][c], v[a][c], dwv[c]);
+            }
+            bstore<CPL, kStream>(dwr, voff, (uint32_t)p * opaque_u32((uint32_t)C * 4u), dwv);
+#pragma unroll
+            for (int a = 0; a < n1; ++a)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    dxa[o1 + a][c] = __builtin_fmaf(wv[p][c], v[a][c], dxa[o1 + a][c]);
+                    pin_f32(dxa[o1 + a][c]);
+                }
+            if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        // (b) B_p[m2] = sum C_p[m1][m2][m3] x[m1] g[m3], m1 outermost
+        float B[kMaxL + 1][2 * kMaxL + 1][CPL];
+        static_for<n1>([&](auto aI) __attribute__((always_inline)) {
+            constexpr int a = decltype(aI)::value;
+            float p3[n3][CPL];
+#pragma unroll
+            for (int b = 0; b < n3; ++b)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) p3[b][c] = xv[o1 + a][c] * gv[o3 + b][c];
+            static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+                constexpr int kk = decltype(kI)::value;
+                constexpr int p = pp.p[kk];
+                constexpr int z0 = nz_m1_begin<S>(p, a), z1 = nz_m1_begin<S>(p, a + 1);
+                static_for<z1 - z0>([&](auto zI) __attribute__((always_inline)) {
+                    constexpr int n = z0 + decltype(zI)::value;
+                    constexpr CgNz nzv = S::nz[n];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        if constexpr (nz_first_m2<S>(n))
+                            B[kk][nzv.m2][c] = nzv.c * p3[nzv.m3][c];
+                        else
+                            B[kk][nzv.m2][c] = __builtin_fmaf(nzv.c, p3[nzv.m3][c], B[kk][nzv.m2][c]);
+                    }
+                });
+            });
+            if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+        });
+        // (c) dY partial sums
+        static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+            constexpr int kk = decltype(kI)::value;
+            constexpr int p = pp.p[kk];
+            constexpr int n2 = 2 * S::paths[p].l2 + 1, o2 = S::paths[p].l2 * S::paths[p].l2;
+#pragma unroll
+            for (int b = 0; b < n2; ++b)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    dya[o2 + b] = __builtin_fmaf(wv[p][c], B[kk][b][c], dya[o2 + b]);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// After an edge: dY summed over the workgroup's channels (lanes by fixed-order
+// halving, then waves through LDS in wave order) while T of the next edge is
+// built into Tn from its harmonics ynext (staged in Yn); wave 0 stores dY of
+// edge e_cur, or with VEC dvec = J(vec)^T dY.  tt is the thread index.
+template <int L, int V, bool VEC>
+__device__ __forceinline__ void edge_dy_finish(const float (&dya)[16], float (*sRed)[16], float* Tn, float* Yn,
+                                               const SlotDev* sTab, const ShCoef* sSh, bool has_next, float ynext,
+                                               int tt, int nth, int nwaves, const float* __restrict__ yv, long e_cur,
+                                               float* __restrict__ dyv) {
+    constexpr int D2 = (L + 1) * (L + 1);
+    const int ln = tt & 63;
+    // dY: lanes (fixed-order halving), then waves (LDS, fixed order)
+    const float r = wave_sum16(dya, ln);
+    if (sum16_holder(ln)) sRed[tt >> 6][sum16_index(ln)] = r;
+    if (has_next && tt < D2) Yn[tt] = ynext;
+    __syncthreads();
+    if (has_next) build_T_lds<L, V>(Tn, Yn, sTab, tt, nth);
+    float tot = 0.0f;
+    if (tt < D2) {
+        tot = sRed[0][tt];
+        for (int q = 1; q < nwaves; ++q) tot += sRed[q][tt];
+    }
+    if constexpr (VEC) {
+        // dvec = (I - r r^T)/|v| * sum_k dY_k grad Y_k(r), lanes < D2 of wave 0
+        if (tt < 64) {
+            const float* vp = yv + 3 * e_cur;
+            const float vx = vp[0], vy = vp[1], vz = vp[2];
+            const float n2 = vx * vx + vy * vy + vz * vz;
+            const float inv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+            const float rx = vx * inv, ry = vy * inv, rz = vz * inv;
+            float g[3] = {0.0f, 0.0f, 0.0f};
+            if (ln < D2) {
+                sh_component_grad_c(sSh[ln], rx, ry, rz, g);
+                g[0] *= tot; g[1] *= tot; g[2] *= tot;
+            }
+            const float gx = lane_value(wave_sum_to_last(g[0]), 63);
+            const float gy = lane_value(wave_sum_to_last(g[1]), 63);
+            const float gz = lane_value(wave_sum_to_last(g[2]), 63);
+            const float rg = rx * gx + ry * gy + rz * gz;
+            if (ln < 3) {
+                const float gl = ln == 0 ? gx : (ln == 1 ? gy : gz);
+                const float rl = ln == 0 ? rx : (ln == 1 ? ry : rz);
+                dyv[3 * e_cur + ln] = (gl - rg * rl) * inv;
+            }
+        }
+    } else {
+        if (tt < D2) dyv[e_cur * D2 + tt] = tot;
+    }
+}
+
+// Harmonics of edge e for the next T build: lane tt < D2 gets Y_e[tt] (from
+// vec and the LDS coefficient copy with VEC, else a buffer load); others 0.
+template <int D2, bool VEC>
+__device__ __forceinline__ float next_y(const float* __restrict__ yv, long e, int tt, const ShCoef* sSh) {
+    if constexpr (VEC) {
+        const float* vp = yv + 3 * e;
+        return tt < D2 ? sh_component_c(tt, sSh[tt < D2 ? tt : 0], vp[0], vp[1], vp[2]) : 0.0f;
+    } else {
+        return sh_load<D2, VEC>(yv, e, tt);
+    }
+}
+
 // With one G slot per path (variant 1) the G row alone is D_out registers per
 // channel, so that variant may take two waves per SIMD instead of spilling.
 // SPLIT (small grids): blockIdx.y picks one half of the sender's out-edges;
@@ -622,6 +781,132 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
 #pragma unroll
         for (int d = 0; d < D1; ++d) bstore<CPL, kStream>(dxr, voff, (uint32_t)(d * C * 4), dxa[d]);
     }
+}
+
+// ------------------------------------------------------------ K3m: receiver-major backward with edge messages
+//
+// The same products as K3 with the roles of the two nodes exchanged: one
+// workgroup per receiver i keeps G[i] in registers and walks its in-edges in
+// CSR order, loading x[j] and w[e] per edge.  dw[e] and dY[e] are stored as in
+// K3; the edge's message msg[e, l1 m1] = sum_p w_p v_p[m1] goes to a workspace
+// row e, and k_msg_sum then forms dx[j] as the sum of the messages of j's
+// out-edges in sender-sorted order (fixed, so reproducible).  G is read once
+// per receiver instead of once per edge, which pays when G's rows are much
+// wider than x's (one output slot per path: 99 against 16 components at L=3).
+
+// x row of sender j and w row of edge e, CPL channels per lane.
+template <class S, int CPL>
+__device__ __forceinline__ void load_recv_operands(float (&xv)[S::D1][CPL], float (&wv)[S::P][CPL],
+                                                   const float* __restrict__ x, const float* __restrict__ w, long j,
+                                                   long e, int C, uint32_t voff) {
+    const rsrc_t xr = make_row(x + j * S::D1 * C, (long)S::D1 * C);
+    const rsrc_t wr = make_row(w + e * S::P * C, (long)S::P * C);
+    const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+#pragma unroll
+    for (int d = 0; d < S::D1; ++d) bload<CPL>(xr, voff, (uint32_t)d * c4, xv[d]);
+#pragma unroll
+    for (int p = 0; p < S::P; ++p) bload<CPL, kStream>(wr, voff, (uint32_t)p * c4, wv[p]);
+}
+
+template <int L, bool VEC, int V>
+__global__ void __launch_bounds__(kBwdMaxThreads)
+__attribute__((amdgpu_waves_per_eu(V == kVariantSlots ? 2 : BWD_WPE, 8)))
+k_bwd_recv(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ yv,
+           const float* __restrict__ w, const int* __restrict__ row_ptr, const int* __restrict__ senders,
+           float* __restrict__ msg, float* __restrict__ dw, float* __restrict__ dyv) {
+    constexpr int CPL = 1;
+    using S = Spec<L, L, L, V>;
+    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::DO, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
+    __shared__ __attribute__((aligned(16))) float sT[2][NTP];
+    __shared__ float sY[2][16];
+    __shared__ float sRed[kBwdMaxThreads / 64][16];
+    __shared__ SlotDev sTab[NT];
+    __shared__ ShCoef sSh[VEC ? 16 : 1];
+
+    const int i = blockIdx.x;
+    const int k0 = row_ptr[i], k1 = row_ptr[i + 1];
+    if (k0 >= k1) return;   // the whole workgroup: no in-edges, nothing to store
+    const int tid = threadIdx.x, nth = blockDim.x;
+    const int nwaves = nth >> 6;
+    const uint32_t voff = opaque_lane(tid < C ? (uint32_t)tid * 4u : kOffLane);   // no channel: loads 0, stores dropped
+
+    float gv[D3][CPL];
+    {
+        const rsrc_t gr = make_row(G + (long)i * D3 * C, (long)D3 * C);
+#pragma unroll
+        for (int d = 0; d < D3; ++d) bload<CPL, kStream>(gr, voff, (uint32_t)(d * C * 4), gv[d]);
+    }
+    {
+        const SlotDev* tab = slot_tab<L, V>();
+        for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
+        if constexpr (VEC)
+            if (tid < 16) sSh[tid] = sh_tab().k[tid];
+    }
+    float xv[D1][CPL], wv[P][CPL];
+    long e = k0;
+    const float y0 = sh_load<D2, VEC>(yv, e, tid);
+    load_recv_operands<S, CPL>(xv, wv, x, w, senders[k0], e, C, voff);
+    if (tid < D2) sY[0][tid] = y0;
+    __syncthreads();
+    build_T_lds<L, V>(sT[0], sY[0], sTab, tid, nth);
+    __syncthreads();
+
+    // Per in-edge: products with T(e) and the rows in registers, the message
+    // stored, then the next edge's rows loaded while dY is reduced and T(e+1)
+    // built in the other buffer.
+    for (int k = k0; k < k1; ++k) {
+        const int buf = (k - k0) & 1;
+        const bool has_next = k + 1 < k1;
+        float mx[D1][CPL], dya[16];
+#pragma unroll
+        for (int d = 0; d < D1; ++d) mx[d][0] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) dya[d] = 0.0f;
+        edge_backward<L, S, CPL>(sT[buf], xv, gv, wv, make_row(dw + e * P * C, (long)P * C), voff, C, mx, dya);
+        {
+            const rsrc_t mr = make_row(msg + e * D1 * C, (long)D1 * C);
+#pragma unroll
+            for (int d = 0; d < D1; ++d) bstore<CPL, kStream>(mr, voff, (uint32_t)(d * C * 4), mx[d]);
+        }
+#pragma unroll
+        for (int d = 0; d < D2; ++d) pin_f32(dya[d]);
+        const long e_cur = e;
+        e = has_next ? k + 1 : k;
+        const int tt = (int)opaque_lane((uint32_t)tid);
+        const float ynext = next_y<D2, VEC>(yv, e, tt, sSh);
+        load_recv_operands<S, CPL>(xv, wv, x, w, senders[e], e, C, has_next ? voff : kOffLane);
+        __builtin_amdgcn_sched_barrier(0);
+        edge_dy_finish<L, V, VEC>(dya, sRed, sT[buf ^ 1], sY[buf ^ 1], sTab, sSh, has_next, ynext, tt, nth, nwaves,
+                                  yv, e_cur, dyv);
+        __syncthreads();
+    }
+}
+
+// dx[j] = sum over j's out-edges k (sender-sorted order) of msg[send_perm[k]]:
+// one workgroup per (sender, span of the row), VW floats per thread, four
+// edges' loads in flight, additions in edge order.
+template <int VW>
+__global__ void __launch_bounds__(256)
+k_msg_sum(long row, const float* __restrict__ msg, const int* __restrict__ send_ptr,
+          const int* __restrict__ send_perm, float* __restrict__ dx) {
+    using vec_t = float __attribute__((ext_vector_type(VW)));
+    const int j = blockIdx.x;
+    const long t = ((long)blockIdx.y * 256 + threadIdx.x) * VW;
+    if (t >= row) return;
+    const int k0 = send_ptr[j], k1 = send_ptr[j + 1];
+    vec_t acc = (vec_t)0.0f;
+    int k = k0;
+    for (; k + 4 <= k1; k += 4) {
+        vec_t m[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            m[q] = __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(msg + (long)send_perm[k + q] * row + t));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc += m[q];
+    }
+    for (; k < k1; ++k)
+        acc += __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(msg + (long)send_perm[k] * row + t));
+    *reinterpret_cast<vec_t*>(dx + (long)j * row + t) = acc;
 }
 
 // ------------------------------------------------------------ standalone harmonics (vec -> Y, dY -> dvec)
@@ -866,6 +1151,35 @@ hipError_t bwd_L(const LaunchArgs& a, hipStream_t st) {
     return bwd_dispatch<L, 1, kVariantSummed>(a, bwd_chan_map(a.C), st);
 }
 
+template <int L, int V>
+hipError_t bwd_msg_L(const LaunchArgs& a, float* msg, hipStream_t st) {
+    const ChanMap m = bwd_chan_map(a.C);
+    if (a.n_edges > 0) {
+        const dim3 grid(a.n_nodes), block(64 * m.waves);
+        if (a.vec_mode)
+            hipLaunchKernelGGL((k_bwd_recv<L, true, V>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w, a.row_ptr,
+                               a.senders, msg, a.dw, a.dy);
+        else
+            hipLaunchKernelGGL((k_bwd_recv<L, false, V>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+                               a.row_ptr, a.senders, msg, a.dw, a.dy);
+    }
+    // dx rows of senders without out-edges come out zero
+    const long row = (long)Spec<L, L, L, V>::D1 * a.C;
+    if (row % 4 == 0)
+        hipLaunchKernelGGL(k_msg_sum<4>, dim3(a.n_nodes, (unsigned)((row + 1023) / 1024)), dim3(256), 0, st, row,
+                           msg, a.send_ptr, a.send_perm, a.dx);
+    else
+        hipLaunchKernelGGL(k_msg_sum<1>, dim3(a.n_nodes, (unsigned)((row + 255) / 256)), dim3(256), 0, st, row, msg,
+                           a.send_ptr, a.send_perm, a.dx);
+    return hipGetLastError();
+}
+
+template <int L>
+hipError_t bwd_msg_V(const LaunchArgs& a, float* msg, hipStream_t st) {
+    if (a.variant == kVariantSlots) return bwd_msg_L<L, kVariantSlots>(a, msg, st);
+    return bwd_msg_L<L, kVariantSummed>(a, msg, st);
+}
+
 }  // namespace
 
 bool bwd_supports_channels(int C) {
@@ -891,6 +1205,17 @@ hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st) {
         case 1: return bwd_L<1>(a, st);
         case 2: return bwd_L<2>(a, st);
         case 3: return bwd_L<3>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_msg(const LaunchArgs& a, float* msg, hipStream_t st) {
+    if (a.n_nodes == 0) return hipSuccess;
+    switch (a.L) {
+        case 0: return bwd_msg_V<0>(a, msg, st);
+        case 1: return bwd_msg_V<1>(a, msg, st);
+        case 2: return bwd_msg_V<2>(a, msg, st);
+        case 3: return bwd_msg_V<3>(a, msg, st);
     }
     return hipErrorInvalidValue;
 }

@@ -47,6 +47,9 @@ hipError_t launch_fwd(const LaunchArgs& a, hipStream_t st);
 hipError_t launch_double_bwd(const DoubleArgs& a, hipStream_t st);
 bool dd_supports_channels(int C);
 hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st);
+// Backward through an edge-message workspace msg[E][D][C]: receiver-major
+// products, then per-sender sums of the messages.
+hipError_t launch_bwd_msg(const LaunchArgs& a, float* msg, hipStream_t st);
 bool bwd_supports_channels(int C);
 hipError_t launch_sh(int L, long n_edges, const float* vec, float* Y, hipStream_t st);
 hipError_t launch_sh_bwd(int L, long n_edges, const float* vec, const float* dY, float* dvec, hipStream_t st);

@@ -191,6 +191,41 @@ def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int =
     return dx, dw, dy
 
 
+def conv_tp_bwd_msg_workspace(n_nodes: int, n_edges: int, channels: int, lmax: int, y_mode: int = Y_GIVEN,
+                              variant: int = SUMMED) -> int:
+    """Bytes of device workspace conv_tp_bwd_msg needs (E * (lmax+1)^2 * C * 4)."""
+    prob = _problem(n_nodes, n_edges, channels, lmax, y_mode, ALGO_CSR, variant)
+    out = ctypes.c_int64(0)
+    check(lib().conv_tp_bwd_msg_workspace(ctypes.byref(prob), ctypes.byref(out)))
+    return out.value
+
+
+def conv_tp_bwd_msg(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN,
+                    dx=None, dw=None, dy=None, variant: int = SUMMED, workspace=None):
+    """conv_tp_bwd through an edge-message workspace (receiver-major products,
+    then per-sender sums; see include/convtp.h).  workspace: a float32 device
+    tensor of at least conv_tp_bwd_msg_workspace bytes, allocated here if None."""
+    n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant)
+    _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
+    send_ptr, send_perm, send_recv = graph.transpose
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w) if dw is None else dw
+    dy = torch.empty_like(y_or_vec) if dy is None else dy
+    _want(dx, "dx", x.shape, device=x.device)
+    _want(dw, "dw", w.shape, device=x.device)
+    _want(dy, "dy", y_or_vec.shape, device=x.device)
+    prob = _problem(n, e, c, lmax, y_mode, ALGO_CSR, variant)
+    if workspace is None:
+        workspace = torch.empty(max(1, e * dim(lmax) * c), dtype=torch.float32, device=x.device)
+    if workspace.dtype != torch.float32 or workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 tensor on x's device")
+    check(lib().conv_tp_bwd_msg(ctypes.byref(prob), _p(grad_out), _p(x), _p(y_or_vec), _p(w),
+                                _p(graph.row_ptr), _p(graph.senders), _p(send_ptr), _p(send_perm),
+                                _p(send_recv), _p(dx), _p(dw), _p(dy), _p(workspace),
+                                workspace.numel() * 4, _stream(x)))
+    return dx, dw, dy
+
+
 def conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph: Graph, lmax: int, out=None):
     """VJP of conv_tp_bwd (Y given): gradients (g_x, g_w, g_y, g_grad) of
     <a_x, dx> + <a_w, dw> + <a_y, dY> (see include/convtp.h)."""

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 101
+    assert L.conv_tp_version() == 102
 
 
 def test_paths_match_oracle(capi):
@@ -124,6 +124,31 @@ def test_bwd_rejections(capi):
         assert _bwd(capi, p, **{k: NUL}) == capi.CTP_EINVAL, k
     assert _bwd(capi, p, dw=MIS) == capi.CTP_EALIGN
     assert _bwd(capi, p, g=MIS) == capi.CTP_EALIGN
+
+
+def _bwd_msg(capi, prob, ws=A2, nbytes=1 << 40, **kw):
+    a = dict(g=A, x=A, y=A, w=A, rp=A, s=A, sp=A, pe=A, sr=A, dx=A2, dw=A2, dy=A2)
+    a.update(kw)
+    return capi.lib().conv_tp_bwd_msg(ctypes.byref(prob), *a.values(), ws, nbytes, NUL)
+
+
+def test_bwd_msg_rejections(capi):
+    L = capi.lib()
+    nb = ctypes.c_int64(-1)
+    p = _prob(capi, n_nodes=4, n_edges=8, channels=16, l_in=2, l_sh=2, l_out=2)
+    assert L.conv_tp_bwd_msg_workspace(ctypes.byref(p), ctypes.byref(nb)) == capi.CTP_OK
+    assert nb.value == 8 * 9 * 16 * 4
+    assert L.conv_tp_bwd_msg_workspace(ctypes.byref(p), None) == capi.CTP_EINVAL
+    assert L.conv_tp_bwd_msg_workspace(ctypes.byref(_prob(capi, variant=3)), ctypes.byref(nb)) == capi.CTP_EINVAL
+    assert len(L.conv_tp_bwd_msg.argtypes) == 16   # problem, 12 arrays, workspace, its size, stream
+    assert _bwd_msg(capi, _prob(capi, algo=1)) == capi.CTP_EUNSUPPORTED
+    assert _bwd_msg(capi, _prob(capi, channels=513)) == capi.CTP_EUNSUPPORTED
+    for k in ("g", "x", "y", "w", "rp", "s", "sp", "pe", "sr", "dx", "dw", "dy"):
+        assert _bwd_msg(capi, p, **{k: NUL}) == capi.CTP_EINVAL, k
+    assert _bwd_msg(capi, p, nbytes=nb.value - 4) == capi.CTP_EINVAL
+    assert "workspace" in L.conv_tp_last_error().decode()
+    assert _bwd_msg(capi, p, ws=NUL, nbytes=nb.value) == capi.CTP_EINVAL
+    assert _bwd_msg(capi, p, ws=MIS, nbytes=nb.value) == capi.CTP_EALIGN
 
 
 def test_node_entry_points_validate(capi):

@@ -498,6 +498,104 @@ def test_variant_slots_full_l3_sampled(ctp, dev):
     close("dY[sample]", host(dy[ei]), dY_ref)
 
 
+# ------------------------------------------------------------ backward through edge messages
+
+
+def run_msg(ctp, dev, d, L, y_mode, variant, ws=None):
+    """conv_tp_bwd_msg against the oracle (dx, dw, dY) and against conv_tp_bwd
+    (dw and dY bitwise: the same per-edge arithmetic)."""
+    n, e = d["n_nodes"], d["n_edges"]
+    prob = oc.Problem(L, L, L, variant=variant)
+    vec = d["vec"]
+    Y = sh32(L, vec)
+    yv = T(Y if y_mode == 0 else vec, dev)
+    Yref = Y.astype(np.float64) if y_mode == 0 else osh.real_sh(L, vec.astype(np.float64))
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w, G = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev)
+    print(f"bwd_msg n={n} e={e} c={x.shape[2]} L={L} y_mode={y_mode} variant={variant}", flush=True)
+    dx, dw, dy = ctp.conv_tp_bwd_msg(G, x, yv, w, g, L, y_mode, variant=variant, workspace=ws)
+    sp, pe, sr = og.transpose(n, d["row_ptr"], d["senders"])
+    close("dx", host(dx), oc.bwd_dx(prob, Yref, d["w"], d["grad_out"], sp, pe, sr), nonzero=e > 0)
+    dw_ref, dY_ref = oc.bwd_edges(prob, d["x"], Yref, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+    close("dw", host(dw), dw_ref, nonzero=e > 0)
+    if y_mode == 0:
+        close("dY", host(dy), dY_ref, nonzero=e > 0)
+    else:
+        close("dvec", host(dy), osh.vec_grad_from_sh_grad(L, vec.astype(np.float64), dY_ref), nonzero=e > 0 and L > 0)
+    dx0, dw0, dy0 = ctp.conv_tp_bwd(G, x, yv, w, g, L, y_mode, variant=variant)
+    assert torch.equal(dw, dw0) and torch.equal(dy, dy0)
+
+
+@pytest.mark.parametrize("n,c,L", [(90, 16, 1), (150, 48, 2), (100, 128, 3), (60, 192, 3), (40, 96, 0),
+                                   (30, 512, 2), (50, 7, 2), (45, 5, 0)])
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("y_mode", [0, 1])
+def test_bwd_msg_small(ctp, dev, n, c, L, variant, y_mode):
+    d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=n + c + L)
+    if variant == 1:
+        d = _variant_inputs(d, L)
+    run_msg(ctp, dev, d, L, y_mode, variant)
+
+
+def test_bwd_msg_edge_cases_and_reused_workspace(ctp, dev):
+    """Hub receiver, isolated nodes, self and duplicate edges, zero vectors;
+    the same workspace reused by a second, smaller call; an empty graph."""
+    rng = np.random.default_rng(31)
+    n, c, L = 40, 128, 3
+    recv = np.concatenate([np.full(700, 3), rng.integers(0, n, size=300)])
+    recv[recv == 17] = 18
+    recv = np.sort(recv)
+    s = rng.integers(0, n, size=recv.size)
+    s[s == 21] = 22
+    s[:10] = recv[:10]
+    s[10:20] = s[20:30]
+    e = recv.size
+    vec = rng.standard_normal((e, 3)).astype(np.float32)
+    vec[::37] = 0.0
+    d = dict(n_nodes=n, n_edges=e, row_ptr=og.row_ptr_from_receivers(recv, n), senders=s.astype(np.int32), vec=vec,
+             x=rng.standard_normal((n, 16, c)).astype(np.float32))
+    d = _variant_inputs(d, L)
+    ws = torch.full((e * 16 * c,), float("nan"), device=dev)
+    for y_mode in (0, 1):
+        run_msg(ctp, dev, d, L, y_mode, 1, ws=ws)
+    small = _variant_inputs(gen.poisson_small(20, c, L, mean_deg=6.0, seed=3), L)
+    run_msg(ctp, dev, small, L, 0, 1, ws=ws)
+    g = ctp.Graph(5, T(np.zeros(6, dtype=np.int32), dev), T(np.zeros(0, dtype=np.int32), dev))
+    x = torch.randn(5, 16, c, device=dev)
+    dx, dw, dy = ctp.conv_tp_bwd_msg(torch.randn(5, 99, c, device=dev), x, torch.empty(0, 16, device=dev),
+                                     torch.empty(0, 23, c, device=dev), g, L, 0, variant=1)
+    assert not dx.any() and dw.numel() == 0 and dy.numel() == 0
+
+
+def test_bwd_msg_full_l3_sampled(ctp, dev):
+    """lmax=3, N=16384, C=128, Poisson(45), Y given, natural-parity paths with
+    slots, as the timed variant-1 backward runs it."""
+    n, c, L = 16384, 128, 3
+    d = gen.poisson_full(n, c, L, dev, seed=0, need_grad=False)
+    pr = oc.Problem(L, L, L, variant=1)
+    rp, s = d["row_ptr"], d["senders"]
+    e = len(s)
+    w = gen.normal_tensor((e, pr.P, c), 0, 21, dev)
+    G = gen.normal_tensor((n, pr.D3, c), 0, 23, dev)
+    Y = sh32(L, d["vec"])
+    g = ctp.Graph(n, T(rp, dev), T(s, dev))
+    print("bwd_msg full l3 variant 1", flush=True)
+    dx, dw, dy = ctp.conv_tp_bwd_msg(G, d["x"], T(Y, dev), w, g, L, 0, variant=1)
+    Yr = Y.astype(np.float64)
+    x_h, G_h = host(d["x"]), host(G)
+    rng = np.random.default_rng(6)
+    rows = np.sort(rng.choice(n, 32, replace=False))
+    close("dx[sample]", host(dx[torch.as_tensor(rows, device=dev)]), _sub_dx(pr, rp, s, Yr, w, G_h, rows))
+    edges = np.sort(rng.choice(e, 128, replace=False))
+    dw_ref, dY_ref = _sub_edges(pr, rp, s, Yr, w, x_h, G_h, edges)
+    ei = torch.as_tensor(edges, device=dev)
+    close("dw[sample]", host(dw[ei]), dw_ref)
+    close("dY[sample]", host(dy[ei]), dY_ref)
+    dx0, dw0, dy0 = ctp.conv_tp_bwd(G, d["x"], T(Y, dev), w, g, L, 0, variant=1)
+    assert torch.equal(dw, dw0) and torch.equal(dy, dy0)
+    close("dx vs conv_tp_bwd", host(dx), host(dx0))
+
+
 # ------------------------------------------------------------ edge-vector VJP of the VJP
 
 
