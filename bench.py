@@ -187,7 +187,7 @@ def workload_l3mace(ctp, torch, dev, args):
     G = gen.normal_tensor((n, shp[5], c), 0, 23, dev)
     g.transpose
     out, dx, dw, dy = torch.empty_like(G), torch.empty_like(x), torch.empty_like(w), torch.empty_like(y)
-    if args.msg:
+    if args.bwd == "msg":
         # backward through edge messages: the workspace is allocated once, outside the timed steps
         ws = torch.empty(ctp.conv_tp_bwd_msg_workspace(n, e, c, L, ctp.Y_GIVEN, V) // 4, dtype=torch.float32,
                          device=dev)
@@ -206,7 +206,7 @@ def workload_l3mace(ctp, torch, dev, args):
     cfg = {"workload": f"MACE variant (natural-parity paths, per-path output slots), lmax=3, N=16384, C=128, "
                        f"E={e}, Poisson(45) in-degree, Y given, fp32",
            "n_nodes": n, "n_edges": e, "channels": c, "lmax": L, "paths": shp[6], "out_dim": shp[5],
-           "backward": "edge messages (conv_tp_bwd_msg)" if args.msg else "sender-major (conv_tp_bwd)"}
+           "backward": "edge messages (conv_tp_bwd_msg)" if args.bwd == "msg" else "sender-major (conv_tp_bwd)"}
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=e, cfg=cfg, cpu=None)
 
 
@@ -461,7 +461,8 @@ def main():
     ap.add_argument("--workload", default="l3fb", choices=sorted(WORKLOADS))
     ap.add_argument("--channels", type=int, default=128, help="sweepC only")
     ap.add_argument("--vec", action="store_true", help="l3fb with edge vectors instead of Y")
-    ap.add_argument("--msg", action="store_true", help="l3mace: backward through edge messages")
+    ap.add_argument("--bwd", choices=("msg", "sender"), default="msg",
+                    help="l3mace: backward through edge messages (conv_tp_bwd_msg) or sender-major (conv_tp_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-nodes", type=int, default=0,
                     help="receivers in the CPU-oracle sample (0: all of them)")

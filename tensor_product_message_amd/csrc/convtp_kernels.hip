@@ -883,30 +883,48 @@ k_bwd_recv(int C, const float* __restrict__ G, const float* __restrict__ x, cons
 }
 
 // dx[j] = sum over j's out-edges k (sender-sorted order) of msg[send_perm[k]]:
-// one workgroup per (sender, span of the row), VW floats per thread, four
-// edges' loads in flight, additions in edge order.
-template <int VW>
+// one workgroup per (sender, span of the row); each thread owns R vectors of
+// VW floats, 256 * VW floats apart, and keeps U edges' loads in flight;
+// additions run in edge order.
+template <int VW, int U, int R>
 __global__ void __launch_bounds__(256)
 k_msg_sum(long row, const float* __restrict__ msg, const int* __restrict__ send_ptr,
           const int* __restrict__ send_perm, float* __restrict__ dx) {
     using vec_t = float __attribute__((ext_vector_type(VW)));
     const int j = blockIdx.x;
-    const long t = ((long)blockIdx.y * 256 + threadIdx.x) * VW;
+    const long t = ((long)blockIdx.y * 256 * R + threadIdx.x) * VW;
     if (t >= row) return;
     const int k0 = send_ptr[j], k1 = send_ptr[j + 1];
-    vec_t acc = (vec_t)0.0f;
+    bool ok[R];
+    vec_t acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        ok[r] = t + (long)r * 256 * VW < row;
+        acc[r] = (vec_t)0.0f;
+    }
+    auto ld = [&](int k, int r) {
+        return __builtin_nontemporal_load(
+            reinterpret_cast<const vec_t*>(msg + (long)send_perm[k] * row + t + (long)r * 256 * VW));
+    };
     int k = k0;
-    for (; k + 4 <= k1; k += 4) {
-        vec_t m[4];
+    for (; k + U <= k1; k += U) {
+        vec_t m[U][R];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            m[q] = __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(msg + (long)send_perm[k + q] * row + t));
+        for (int q = 0; q < U; ++q)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc += m[q];
+            for (int r = 0; r < R; ++r) m[q][r] = ok[r] ? ld(k + q, r) : (vec_t)0.0f;
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] += m[q][r];
     }
     for (; k < k1; ++k)
-        acc += __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(msg + (long)send_perm[k] * row + t));
-    *reinterpret_cast<vec_t*>(dx + (long)j * row + t) = acc;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (ok[r]) acc[r] += ld(k, r);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (ok[r]) *reinterpret_cast<vec_t*>(dx + (long)j * row + t + (long)r * 256 * VW) = acc[r];
 }
 
 // ------------------------------------------------------------ standalone harmonics (vec -> Y, dY -> dvec)
@@ -1165,12 +1183,15 @@ hipError_t bwd_msg_L(const LaunchArgs& a, float* msg, hipStream_t st) {
     }
     // dx rows of senders without out-edges come out zero
     const long row = (long)Spec<L, L, L, V>::D1 * a.C;
+    // four edges in flight, one vector per thread: eight or sixteen edges, or
+    // two vectors per thread, measured the same at lmax 3, C 128
+    constexpr int kU = 4, kR = 1;
     if (row % 4 == 0)
-        hipLaunchKernelGGL(k_msg_sum<4>, dim3(a.n_nodes, (unsigned)((row + 1023) / 1024)), dim3(256), 0, st, row,
-                           msg, a.send_ptr, a.send_perm, a.dx);
+        hipLaunchKernelGGL((k_msg_sum<4, kU, kR>), dim3(a.n_nodes, (unsigned)((row + 1024 * kR - 1) / (1024 * kR))),
+                           dim3(256), 0, st, row, msg, a.send_ptr, a.send_perm, a.dx);
     else
-        hipLaunchKernelGGL(k_msg_sum<1>, dim3(a.n_nodes, (unsigned)((row + 255) / 256)), dim3(256), 0, st, row, msg,
-                           a.send_ptr, a.send_perm, a.dx);
+        hipLaunchKernelGGL((k_msg_sum<1, kU, kR>), dim3(a.n_nodes, (unsigned)((row + 256 * kR - 1) / (256 * kR))),
+                           dim3(256), 0, st, row, msg, a.send_ptr, a.send_perm, a.dx);
     return hipGetLastError();
 }
 
