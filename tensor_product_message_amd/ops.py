@@ -351,21 +351,25 @@ def conv_tp_bwd_bwd_vec(grad_out, x, vec, w, a_x, a_w, a_vec, graph: Graph, lmax
 
 
 class ConvTPFunction(torch.autograd.Function):
-    """Autograd wrapper: forward = conv_tp_fwd (algo 0), backward = conv_tp_bwd."""
+    """Autograd wrapper: forward = conv_tp_fwd (algo 0); backward = conv_tp_bwd
+    (variant 0) or conv_tp_bwd_msg with a workspace from torch's allocator
+    (variant 1, whose grad_out rows are much wider than x's)."""
 
     @staticmethod
-    def forward(ctx, x, y_or_vec, w, graph, lmax, y_mode):
+    def forward(ctx, x, y_or_vec, w, graph, lmax, y_mode, variant):
         ctx.save_for_backward(x, y_or_vec, w)
-        ctx.graph, ctx.lmax, ctx.y_mode = graph, lmax, y_mode
-        return conv_tp_fwd(x, y_or_vec, w, graph, lmax, y_mode)
+        ctx.graph, ctx.lmax, ctx.y_mode, ctx.variant = graph, lmax, y_mode, variant
+        return conv_tp_fwd(x, y_or_vec, w, graph, lmax, y_mode, variant=variant)
 
     @staticmethod
     def backward(ctx, grad_out):
         x, y_or_vec, w = ctx.saved_tensors
-        dx, dw, dy = conv_tp_bwd(grad_out.contiguous(), x, y_or_vec, w, ctx.graph, ctx.lmax, ctx.y_mode)
-        return dx, dy, dw, None, None, None
+        bwd = conv_tp_bwd_msg if ctx.variant == SLOTS else conv_tp_bwd
+        dx, dw, dy = bwd(grad_out.contiguous(), x, y_or_vec, w, ctx.graph, ctx.lmax, ctx.y_mode,
+                         variant=ctx.variant)
+        return dx, dy, dw, None, None, None, None
 
 
-def conv_tp(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN):
+def conv_tp(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN, variant: int = SUMMED):
     """Differentiable fused convolution tensor product."""
-    return ConvTPFunction.apply(x, y_or_vec, w, graph, lmax, y_mode)
+    return ConvTPFunction.apply(x, y_or_vec, w, graph, lmax, y_mode, variant)

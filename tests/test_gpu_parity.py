@@ -596,6 +596,38 @@ def test_bwd_msg_full_l3_sampled(ctp, dev):
     close("dx vs conv_tp_bwd", host(dx), host(dx0))
 
 
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("y_mode", [0, 1])
+def test_autograd_wrapper(ctp, dev, variant, y_mode):
+    """conv_tp (torch.autograd) gives the library's forward and the oracle's
+    gradients of <G, out> in x, w and Y (or vec)."""
+    L = 2
+    d = gen.poisson_small(80, 64, L, mean_deg=10.0, seed=41)
+    if variant == 1:
+        d = _variant_inputs(d, L)
+    n = d["n_nodes"]
+    prob = oc.Problem(L, L, L, variant=variant)
+    vec = d["vec"]
+    Y = sh32(L, vec)
+    Yref = Y.astype(np.float64) if y_mode == 0 else osh.real_sh(L, vec.astype(np.float64))
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x = T(d["x"], dev).requires_grad_(True)
+    w = T(d["w"], dev).requires_grad_(True)
+    yv = T(Y if y_mode == 0 else vec, dev).requires_grad_(True)
+    print(f"autograd variant={variant} y_mode={y_mode}", flush=True)
+    out = ctp.conv_tp(x, yv, w, g, L, y_mode, variant=variant)
+    (out * T(d["grad_out"], dev)).sum().backward()
+    close("out", host(out), oc.fwd(prob, d["x"], Yref, d["w"], d["row_ptr"], d["senders"]))
+    sp, pe, sr = og.transpose(n, d["row_ptr"], d["senders"])
+    close("x.grad", host(x.grad), oc.bwd_dx(prob, Yref, d["w"], d["grad_out"], sp, pe, sr))
+    dw_ref, dY_ref = oc.bwd_edges(prob, d["x"], Yref, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+    close("w.grad", host(w.grad), dw_ref)
+    if y_mode == 0:
+        close("Y.grad", host(yv.grad), dY_ref)
+    else:
+        close("vec.grad", host(yv.grad), osh.vec_grad_from_sh_grad(L, vec.astype(np.float64), dY_ref))
+
+
 # ------------------------------------------------------------ edge-vector VJP of the VJP
 
 
