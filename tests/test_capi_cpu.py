@@ -4,6 +4,7 @@ every invalid argument on the host before any HIP call."""
 import ctypes
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -240,6 +241,33 @@ def test_other_entry_points_validate(capi):
     assert L.conv_tp_stream_probe(1, NUL, NUL, 16, NUL) == capi.CTP_EINVAL
     assert L.conv_tp_stream_probe(0, MIS, A2, 16, NUL) == capi.CTP_EALIGN
     assert L.conv_tp_stream_probe(2, A, A2, 0, NUL) == capi.CTP_OK
+
+
+def test_header_is_plain_c99(tmp_path):
+    src = tmp_path / "h.c"
+    src.write_text('#include "convtp.h"\nint f(void) { return CTP_OK + (int)sizeof(conv_tp_problem); }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_c_consumer_builds_and_reports_bad_input(capi, tmp_path):
+    """The C99 consumer of the ABI compiles warning-free (built here into a
+    temporary directory) and fails cleanly, before any device work, on input
+    it cannot read."""
+    exe = tmp_path / "roundtrip"
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    lib_dir = os.path.dirname(capi.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"),
+                        os.path.join(ROOT, "tests", "c_abi", "roundtrip.c"), "-o", str(exe),
+                        "-L", lib_dir, "-lconvtp", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+                        "-Wl,-rpath," + lib_dir, "-Wl,-rpath," + os.path.join(rocm, "lib")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe), str(tmp_path / "missing.bin"), str(tmp_path / "o.bin")],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "cannot open input" in r.stderr
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

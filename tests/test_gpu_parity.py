@@ -149,6 +149,51 @@ def test_deterministic_reruns(ctp, dev):
             assert torch.equal(u, v)
 
 
+@pytest.mark.parametrize("n,c", [(300, 128), (4096, 64)])
+def test_hip_graph_replays(ctp, dev, n, c):
+    """The forward and both backward entry points enqueue kernels only, so a
+    HIP graph (torch.cuda.graph) captures them; every replay, with eager work
+    on the outputs in between, gives the eager results bitwise.  (300, 128)
+    takes the small-grid split, whose zeroing is a kernel, not a memset;
+    (4096, 64) the unsplit path."""
+    L = 3
+    d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=n + c)
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    g.transpose
+    x, w, G = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev)
+    y = T(sh32(L, d["vec"]), dev)
+    e = d["n_edges"]
+    ws = torch.empty(e * 16 * c, device=dev)
+    outs = [torch.empty_like(x)] + [torch.empty_like(t) for t in (x, w, y)] + [torch.empty_like(t) for t in (x, w, y)]
+
+    def run():
+        ctp.conv_tp_fwd(x, y, w, g, L, 0, out=outs[0])
+        ctp.conv_tp_bwd(G, x, y, w, g, L, 0, dx=outs[1], dw=outs[2], dy=outs[3])
+        ctp.conv_tp_bwd_msg(G, x, y, w, g, L, 0, dx=outs[4], dw=outs[5], dy=outs[6], workspace=ws)
+
+    print(f"graph capture n={n} c={c}", flush=True)
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for k in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "dx", "dw", "dY", "dx msg", "dw msg", "dY msg"), outs, ref):
+            assert torch.equal(a, b), (k, name)
+
+
 # ------------------------------------------------------------ bookkeeping and harmonics
 
 
