@@ -174,7 +174,8 @@ k_dd_recv(int C, const float* __restrict__ x, const float* __restrict__ ax, cons
 // Per out-edge e = j -> i with g = G[i], for each (l1, l3) pair:
 //   v_p = T_p(Y)^T g,  v'_p = T_p(aY)^T g
 //   gw[e,p] = ax . v_p + x . v'_p,   gx[j] += aw_p v_p + w_p v'_p
-//   gY[e, l2 m2] = sum_c sum_p w_p B_p(ax, g)[m2] + aw_p B_p(x, g)[m2],
+//   gY[e, l2 m2] = sum_c sum_p w_p B_p(ax, g)[m2] + aw_p B_p(x, g)[m2]
+//                = sum_c sum_p B_p(w_p ax + aw_p x, g)[m2]   (B is linear in a),
 //   B_p(a, g)[m2] = sum_{m1,m3} C_p[m1][m2][m3] a[m1] g[m3].
 
 template <int L>
@@ -282,40 +283,33 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
                             if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
                         });
                         __builtin_amdgcn_sched_barrier(0);
-                        // (b) gY: B_p(ax, g) weighted by w, then B_p(x, g) weighted by aw
-                        auto bphase = [&](const float(&av)[D1], const float(&wsel)[P]) __attribute__((always_inline)) {
-                            float B[kMaxL + 1][2 * kMaxL + 1];
+                        // (b) gY per path: u_p = w_p ax + aw_p x, then B_p(u_p, g) added into gY.
+                        // Weighting before the contraction halves the coupling work: at L=3
+                        // 1,620 instead of 2,046 operations per (edge, channel) for gY.
+                        static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+                            constexpr int p = pp.p[decltype(kI)::value];
+                            constexpr int n2 = 2 * S::paths[p].l2 + 1, o2 = S::paths[p].l2 * S::paths[p].l2;
+                            float u[n1], B[2 * kMaxL + 1];
+#pragma unroll
+                            for (int q = 0; q < n1; ++q) u[q] = __builtin_fmaf(awv[p], xv[o1 + q], wv[p] * axv[o1 + q]);
                             static_for<n1>([&](auto aI) __attribute__((always_inline)) {
-                                constexpr int a = decltype(aI)::value;
-                                float p3[n3];
-#pragma unroll
-                                for (int b = 0; b < n3; ++b) p3[b] = av[o1 + a] * gv[o3 + b];
-                                static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
-                                    constexpr int kk = decltype(kI)::value;
-                                    constexpr int p = pp.p[kk];
-                                    constexpr int z0 = nz_m1_begin<S>(p, a), z1 = nz_m1_begin<S>(p, a + 1);
-                                    static_for<z1 - z0>([&](auto zI) __attribute__((always_inline)) {
-                                        constexpr int n = z0 + decltype(zI)::value;
-                                        constexpr CgNz nzv = S::nz[n];
-                                        if constexpr (nz_first_m2<S>(n))
-                                            B[kk][nzv.m2] = nzv.c * p3[nzv.m3];
-                                        else
-                                            B[kk][nzv.m2] = __builtin_fmaf(nzv.c, p3[nzv.m3], B[kk][nzv.m2]);
-                                    });
+                                constexpr int q = decltype(aI)::value;
+                                constexpr int z0 = nz_m1_begin<S>(p, q), z1 = nz_m1_begin<S>(p, q + 1);
+                                static_for<z1 - z0>([&](auto zI) __attribute__((always_inline)) {
+                                    constexpr int n = z0 + decltype(zI)::value;
+                                    constexpr CgNz nzv = S::nz[n];
+                                    const float prod = u[q] * gv[o3 + nzv.m3];
+                                    if constexpr (nz_first_m2<S>(n))
+                                        B[nzv.m2] = nzv.c * prod;
+                                    else
+                                        B[nzv.m2] = __builtin_fmaf(nzv.c, prod, B[nzv.m2]);
                                 });
-                                if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
                             });
-                            static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
-                                constexpr int kk = decltype(kI)::value;
-                                constexpr int p = pp.p[kk];
-                                constexpr int n2 = 2 * S::paths[p].l2 + 1, o2 = S::paths[p].l2 * S::paths[p].l2;
 #pragma unroll
-                                for (int b = 0; b < n2; ++b) gya[o2 + b] = __builtin_fmaf(wsel[p], B[kk][b], gya[o2 + b]);
-                            });
-                            __builtin_amdgcn_sched_barrier(0);
-                        };
-                        bphase(axv, wv);
-                        bphase(xv, awv);
+                            for (int q = 0; q < n2; ++q) gya[o2 + q] += B[q];
+                            if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+                        });
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 });
             });
