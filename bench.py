@@ -211,6 +211,40 @@ def workload_l3mace(ctp, torch, dev, args):
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=e, cfg=cfg, cpu=None)
 
 
+def workload_gather(ctp, torch, dev, args):
+    """Cache-footprint diagnostic at the lmax=3 step's sizes: the forward on a
+    graph whose senders are nodes 0..K-1 and the backward on one whose
+    receivers are nodes 0..K-1 (K = --gather-nodes), so the per-edge row
+    gathers (x, then G) come from K rows of 8 KB; w, dw and the other streams
+    are those of the real workload."""
+    from workloads import gen
+    L, n, c, k = 3, 16384, 128, args.gather_nodes
+    (rp_a, s_a), (rp_b, s_b) = gen.gather_limited_graphs(n, 45.0, k, gen.rng_for(0))
+    e = len(s_a)
+    ga = ctp.Graph(n, torch.as_tensor(rp_a).to(dev), torch.as_tensor(s_a).to(dev))
+    gb = ctp.Graph(n, torch.as_tensor(rp_b).to(dev), torch.as_tensor(s_b).to(dev))
+    gb.transpose
+    x = gen.normal_tensor((n, 16, c), 0, 1, dev)
+    w = gen.normal_tensor((e, ctp.num_paths(L), c), 0, 2, dev)
+    G = gen.normal_tensor((n, 16, c), 0, 3, dev)
+    vec = torch.as_tensor(gen.unit_vectors(e, gen.rng_for(1))).to(dev)
+    y = ctp.spherical_harmonics(vec, L)
+    out, dx, dw, dy = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w), torch.empty_like(y)
+    torch.cuda.synchronize()
+
+    def step(t):
+        t.run("fwd", lambda: ctp.conv_tp_fwd(x, y, w, ga, L, ctp.Y_GIVEN, out=out))
+        t.run("bwd", lambda: ctp.conv_tp_bwd(G, x, y, w, gb, L, ctp.Y_GIVEN, dx=dx, dw=dw, dy=dy))
+
+    d = dict(n_nodes=n, n_edges=e, channels=c)
+    shp = shape_of(d, ctp, L, ctp.Y_GIVEN)
+    kb = {"fwd": fwd_bytes(*shp), "bwd": bwd_bytes(*shp)}
+    cfg = {"workload": f"gather-footprint diagnostic: lmax=3, N=16384, C=128, E={e}, node-row gathers "
+                       f"limited to {k} nodes ({k * 16 * c * 4 / 2**20:.1f} MiB), Y given, fp32",
+           "n_nodes": n, "n_edges": e, "channels": c, "lmax": L, "gather_nodes": k}
+    return dict(step=step, kernel_bytes=kb, dominant="bwd", edges=e, cfg=cfg, cpu=None)
+
+
 def workload_l2fwd(ctp, torch, dev, args):
     L, y_mode = 2, ctp.Y_GIVEN
     d, g, y = make_poisson(ctp, torch, dev, 32768, 128, L, y_mode, False)
@@ -384,7 +418,8 @@ def workload_hbm(ctp, torch, dev, args):
 
 WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
              "water": workload_water, "tiny": workload_tiny, "copy": workload_copy, "hbm": workload_hbm,
-             "node3": workload_node, "l3dd": workload_l3dd, "l3mace": workload_l3mace}
+             "node3": workload_node, "l3dd": workload_l3dd, "l3mace": workload_l3mace,
+             "gather": workload_gather}
 
 
 # ------------------------------------------------------------ CPU baseline (oracle)
@@ -461,6 +496,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="l3fb", choices=sorted(WORKLOADS))
     ap.add_argument("--channels", type=int, default=128, help="sweepC only")
+    ap.add_argument("--gather-nodes", type=int, default=64, help="gather only: nodes the row gathers touch")
     ap.add_argument("--vec", action="store_true", help="l3fb with edge vectors instead of Y")
     ap.add_argument("--bwd", choices=("msg", "sender"), default="msg",
                     help="l3mace: backward through edge messages (conv_tp_bwd_msg) or sender-major (conv_tp_bwd)")

@@ -64,6 +64,24 @@ def poisson_graph(n_nodes: int, mean_deg: float, rng: np.random.Generator):
     return row_ptr, s.astype(np.int32)
 
 
+def gather_limited_graphs(n_nodes: int, mean_deg: float, k: int, rng: np.random.Generator):
+    """Two graphs of the Poisson workload's size whose node-row gathers touch
+    only nodes 0..k-1 (a cache-footprint diagnostic, not a workload of the
+    method): (a) Poisson(mean_deg) in-degrees over all receivers with senders
+    uniform over 0..k-1, so the forward gathers x from k rows; (b) as many
+    edges with receivers uniform over 0..k-1 (CSR order) and senders uniform
+    over all nodes, so the backward gathers G from k rows.  Self-edges are
+    allowed.  Returns ((row_ptr, senders), (row_ptr, senders))."""
+    deg = rng.poisson(mean_deg, size=n_nodes).astype(np.int64)
+    rp_a = csr_from_degrees(deg)
+    e = int(rp_a[-1])
+    s_a = rng.integers(0, k, size=e, dtype=np.int64).astype(np.int32)
+    recv_b = np.sort(rng.integers(0, k, size=e, dtype=np.int64))
+    rp_b = csr_from_degrees(np.bincount(recv_b, minlength=n_nodes).astype(np.int64))
+    s_b = rng.integers(0, n_nodes, size=e, dtype=np.int64).astype(np.int32)
+    return (rp_a, s_a), (rp_b, s_b)
+
+
 def distinct_sender_graph(n_nodes: int, deg: int, rng: np.random.Generator):
     """Every receiver gets `deg` distinct senders drawn from the other nodes."""
     if deg > n_nodes - 1:
