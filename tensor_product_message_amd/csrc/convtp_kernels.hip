@@ -13,8 +13,9 @@
 // edges in CSR-by-receiver order.
 //
 // Mapping: one workgroup per receiver (forward) or sender (backward) and per
-// channel tile; a lane owns channels c0 + 64 c, c < CPL (CPL = 1 or 2), so
-// every wave-wide access covers 256 contiguous bytes.  Per edge, T_{p,e} is
+// channel tile; a lane owns CPL consecutive channels (CPL = 1 or 2), so every
+// wave-wide access covers 64 * CPL contiguous floats with one dword or dwordx2
+// per lane.  Per edge, T_{p,e} is
 // shared by every channel: the workgroup builds it once in LDS (lane-parallel,
 // <= 2 terms per entry) and every lane then reads it by broadcast.  The path
 // loops are unrolled at compile time over the constexpr tables, so each
@@ -241,8 +242,8 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
 
     const int i = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
-    // lane owns channels c0 + 64 c, c < CPL (a wave covers 64 * CPL channels)
-    const int c0 = blockIdx.y * nth * CPL + (tid >> 6) * 64 * CPL + (tid & 63);
+    // lane owns channels c0 .. c0 + CPL - 1 (a wave covers 64 * CPL channels)
+    const int c0 = blockIdx.y * nth * CPL + (tid >> 6) * 64 * CPL + (tid & 63) * CPL;
     const uint32_t voff = opaque_lane(c0 < C ? (uint32_t)c0 * 4u : kOffLane);
 
     float acc[D3][CPL];
@@ -300,7 +301,7 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
 #pragma unroll
             for (int d = 0; d < D3; ++d)
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + 64 * c, acc[d][c]);
+                for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + c, acc[d][c]);
         }
     } else {
         const rsrc_t orow = make_row(out + (long)i * D3 * C, (long)D3 * C);
@@ -329,7 +330,7 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
 
     const long e = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
-    const int c0 = blockIdx.y * nth * CPL + (tid >> 6) * 64 * CPL + (tid & 63);
+    const int c0 = blockIdx.y * nth * CPL + (tid >> 6) * 64 * CPL + (tid & 63) * CPL;
     const bool active = c0 < C;
     const uint32_t voff = opaque_lane(active ? (uint32_t)c0 * 4u : kOffLane);
 
@@ -358,7 +359,7 @@ k_fwd_atomic(int n_nodes, int C, const float* __restrict__ x, const float* __res
 #pragma unroll
         for (int d = 0; d < D3; ++d)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + 64 * c, acc[d][c]);
+            for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + c, acc[d][c]);
     }
 }
 
@@ -774,7 +775,7 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
 #pragma unroll
             for (int d = 0; d < D1; ++d)
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + 64 * c, dxa[d][c]);
+                for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(o + (long)d * C + c, dxa[d][c]);
         }
     } else {
         const rsrc_t dxr = make_row(dx + (long)j * D1 * C, (long)D1 * C);

@@ -349,49 +349,32 @@ __device__ __forceinline__ uint32_t opaque_lane(uint32_t v) {
 // short-lived instead of deferring every accumulation to the loop latch).
 __device__ __forceinline__ void pin_f32(float& v) { asm volatile("" : "+v"(v)); }
 
-// A lane owns channels c0 + 64 * c (c < CPL): every access instruction then
-// covers 64 consecutive floats (256 contiguous bytes), and channel c's extra
-// 256 bytes go into the scalar offset.
+// A lane owns CPL consecutive channels c0 .. c0 + CPL - 1 (c0 = CPL * lane
+// within the wave's block): one access instruction covers the wave's 64 * CPL
+// consecutive floats (256 or 512 contiguous bytes), one dword or dwordx2 per
+// lane.
 // Cache policy of a buffer access: kStream (non-temporal) marks the edge
-// streams w and dw, which are touched exactly once, so that they do not evict
-// the gathered node rows that later edges read again.
+// streams touched exactly once (w, dw, out, dx).
 constexpr int kCached = 0;
 constexpr int kStream = 2;
 
 template <int CPL, int Aux = kCached>
 __device__ __forceinline__ void bload(rsrc_t r, uint32_t voff, uint32_t soff, float (&v)[CPL]) {
+    static_assert(CPL == 1 || CPL == 2, "one or two channels per lane");
+    // Two adjacent dword loads, which the backend merges into one dwordx2.  (This
+    // compiler narrows __builtin_amdgcn_raw_buffer_load_b64 to a single dword
+    // when its two halves are used apart, so that builtin is not used.)
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
-        v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff + 256u * c, Aux));
+        v[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4u * c, soff, Aux));
 }
 
 template <int CPL, int Aux = kCached>
 __device__ __forceinline__ void bstore(rsrc_t r, uint32_t voff, uint32_t soff, const float (&v)[CPL]) {
+    static_assert(CPL == 1 || CPL == 2, "one or two channels per lane");
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v[c]), r, voff, soff + 256u * c, Aux);
-}
-
-// ------------------------------------------------------------ vector loads
-
-template <int CPL>
-__device__ __forceinline__ void load_ch(const float* __restrict__ p, float (&v)[CPL]) {
-    if constexpr (CPL == 2) {
-        const float2 t = *reinterpret_cast<const float2*>(p);
-        v[0] = t.x;
-        v[1] = t.y;
-    } else {
-        v[0] = p[0];
-    }
-}
-
-template <int CPL>
-__device__ __forceinline__ void store_ch(float* __restrict__ p, const float (&v)[CPL]) {
-    if constexpr (CPL == 2) {
-        *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
-    } else {
-        p[0] = v[0];
-    }
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v[c]), r, voff + 4u * c, soff, Aux);
 }
 
 // ------------------------------------------------------------ per-edge coupling T in LDS
