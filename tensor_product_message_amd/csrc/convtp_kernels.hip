@@ -1062,14 +1062,13 @@ struct ChanMap {
     int cpl, waves, tiles;   // channels per lane, waves per workgroup, channel tiles (grid.y)
 };
 
-// Two channels per lane halve the per-edge overhead (T, loop control) per
-// channel but need twice the registers, so one wave fewer per SIMD; they pay
-// only when the grid has enough rows to fill the chip with fewer waves.
-constexpr long kRowsForTwoChannels = 8192;
-
-ChanMap chan_map(int C, int max_waves, long rows) {
+// One channel per lane.  The kernels also take two adjacent channels per lane
+// (CPL = 2: half the T reads and loop control per channel, twice the
+// registers); measured at C = 128-1024 that was 1-2% slower in the CSR
+// forward and twice as slow in the atomic one, so every launch uses CPL = 1.
+ChanMap chan_map(int C, int max_waves) {
     ChanMap m{};
-    m.cpl = (C % 128 == 0 && rows >= kRowsForTwoChannels) ? 2 : 1;
+    m.cpl = 1;
     const int per_wave = 64 * m.cpl;
     const int need = (C + per_wave - 1) / per_wave;
     m.waves = need < max_waves ? need : max_waves;
@@ -1146,14 +1145,9 @@ hipError_t bwd_dispatch(const LaunchArgs& a, const ChanMap& m, hipStream_t st) {
 
 template <int L>
 hipError_t fwd_L(const LaunchArgs& a, hipStream_t st) {
-    ChanMap m = chan_map(a.C, kMaxThreads / 64, a.algo == 0 ? (long)a.n_nodes : a.n_edges);
-    if (a.variant == kVariantSlots) {
-        // one output slot per path: the accumulators alone take D_out registers
-        // per channel, so one channel per lane
-        if (m.cpl == 2) m = chan_map(a.C, kMaxThreads / 64, 0);
-        return fwd_dispatch<L, 1, kVariantSlots>(a, m, st);
-    }
-    return m.cpl == 2 ? fwd_dispatch<L, 2, kVariantSummed>(a, m, st) : fwd_dispatch<L, 1, kVariantSummed>(a, m, st);
+    const ChanMap m = chan_map(a.C, kMaxThreads / 64);
+    if (a.variant == kVariantSlots) return fwd_dispatch<L, 1, kVariantSlots>(a, m, st);
+    return fwd_dispatch<L, 1, kVariantSummed>(a, m, st);
 }
 
 ChanMap bwd_chan_map(int C) {

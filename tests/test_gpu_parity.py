@@ -117,10 +117,9 @@ def test_small_poisson(ctp, dev, n, c, L, y_mode):
 
 @pytest.mark.parametrize("L", [2, 3])
 @pytest.mark.parametrize("y_mode", [0, 1])
-def test_two_channels_per_lane(ctp, dev, L, y_mode):
-    # C = 128 with at least 8192 receivers takes the forward's two-channels-per-lane
-    # mapping (smaller grids use one channel per lane); a sparse graph keeps the
-    # element-by-element oracle comparison fast.
+def test_many_receivers(ctp, dev, L, y_mode):
+    # 8192 receivers at C = 128 (16384 forward waves, the full-size grid's
+    # shape), element by element; a sparse graph keeps the oracle fast.
     d = gen.poisson_small(8192, 128, L, mean_deg=3.0, seed=7 + L)
     run_small(ctp, dev, d, L, y_mode, 0, bwd=False)
 
