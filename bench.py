@@ -134,8 +134,12 @@ def workload_l3fb(ctp, torch, dev, args):
     dx, dw, dy = torch.empty_like(x), torch.empty_like(w), torch.empty_like(y)
     shp = shape_of(d, ctp, L, y_mode)
 
+    if args.frame and not args.vec:
+        raise SystemExit("--frame needs --vec (the edge-frame forward takes edge vectors)")
+    fwd_algo = ctp.ALGO_FRAME if args.frame else ctp.ALGO_CSR
+
     def step(t):
-        t.run("fwd", lambda: ctp.conv_tp_fwd(x, y, w, g, L, y_mode, out=out))
+        t.run("fwd", lambda: ctp.conv_tp_fwd(x, y, w, g, L, y_mode, fwd_algo, out=out))
         t.run("bwd", lambda: ctp.conv_tp_bwd(G, x, y, w, g, L, y_mode, dx=dx, dw=dw, dy=dy))
 
     kb = {"fwd": fwd_bytes(*shp), "bwd": bwd_bytes(*shp)}
@@ -144,7 +148,8 @@ def workload_l3fb(ctp, torch, dev, args):
     cfg = {"workload": f"lmax=3 conv TP forward+backward, N=16384, C=128, E={shp[1]}, "
                        f"Poisson(45) in-degree, {'vec' if args.vec else 'Y'} given, fp32",
            "n_nodes": shp[0], "n_edges": shp[1], "channels": 128, "lmax": 3,
-           "y_mode": "vec" if args.vec else "Y", "paths": shp[6]}
+           "y_mode": "vec" if args.vec else "Y", "paths": shp[6],
+           "forward": "edge frame (algo 2)" if args.frame else "direct (algo 0)"}
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=shp[1], cfg=cfg,
                 cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=True))
 
@@ -298,9 +303,11 @@ def workload_water(ctp, torch, dev, args):
     dv1, dv2 = torch.empty_like(v), torch.empty_like(v)
     torch.cuda.synchronize()
 
+    fwd_algo = ctp.ALGO_FRAME if args.frame else ctp.ALGO_CSR
+
     def step(t):
-        t.run("fwd1", lambda: ctp.conv_tp_fwd(x0, v, w1, g, L, y_mode, out=h1))
-        t.run("fwd2", lambda: ctp.conv_tp_fwd(h1, v, w2, g, L, y_mode, out=h2))
+        t.run("fwd1", lambda: ctp.conv_tp_fwd(x0, v, w1, g, L, y_mode, fwd_algo, out=h1))
+        t.run("fwd2", lambda: ctp.conv_tp_fwd(h1, v, w2, g, L, y_mode, fwd_algo, out=h2))
         t.run("bwd2", lambda: ctp.conv_tp_bwd(G, h1, v, w2, g, L, y_mode, dx=dh1, dw=dw2, dy=dv2))
         t.run("bwd1", lambda: ctp.conv_tp_bwd(dh1, x0, v, w1, g, L, y_mode, dx=dx0, dw=dw1, dy=dv1))
 
@@ -309,7 +316,8 @@ def workload_water(ctp, torch, dev, args):
     kb = {"fwd1": fwd_bytes(*shp), "fwd2": fwd_bytes(*shp), "bwd1": bwd_bytes(*shp), "bwd2": bwd_bytes(*shp)}
     cfg = {"workload": f"water-box-shaped step: 1503 atoms, {E} edges (10% zero-weight padding), "
                        "C=128, lmax=3, vec given, two layers forward + backward to edge vectors, fp32",
-           "n_nodes": n, "n_edges": E, "channels": 128, "lmax": 3, "layers": 2}
+           "n_nodes": n, "n_edges": E, "channels": 128, "lmax": 3, "layers": 2,
+           "forward": "edge frame (algo 2)" if args.frame else "direct (algo 0)"}
     return dict(step=step, kernel_bytes=kb, dominant="bwd1", edges=E, cfg=cfg, cpu=None)
 
 
@@ -498,6 +506,8 @@ def main():
     ap.add_argument("--channels", type=int, default=128, help="sweepC only")
     ap.add_argument("--gather-nodes", type=int, default=64, help="gather only: nodes the row gathers touch")
     ap.add_argument("--vec", action="store_true", help="l3fb with edge vectors instead of Y")
+    ap.add_argument("--frame", action="store_true",
+                    help="l3fb --vec and water: the forward in each edge's frame (algo 2)")
     ap.add_argument("--bwd", choices=("msg", "sender"), default="msg",
                     help="l3mace: backward through edge messages (conv_tp_bwd_msg) or sender-major (conv_tp_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -72,7 +72,7 @@ int check_problem(const conv_tp_problem* pr, Shape* s) {
     if (pr->l_in != pr->l_sh || pr->l_sh != pr->l_out)
         return fail(CTP_EUNSUPPORTED, "degrees (%d,%d,%d) must be equal in this build", pr->l_in, pr->l_sh, pr->l_out);
     if (pr->y_mode != 0 && pr->y_mode != 1) return fail(CTP_EINVAL, "y_mode = %d not 0 or 1", pr->y_mode);
-    if (pr->algo != 0 && pr->algo != 1) return fail(CTP_EINVAL, "algo = %d not 0 or 1", pr->algo);
+    if (pr->algo < 0 || pr->algo > 2) return fail(CTP_EINVAL, "algo = %d not 0, 1 or 2", pr->algo);
     if (pr->variant != ctp::kVariantSummed && pr->variant != ctp::kVariantSlots)
         return fail(CTP_EINVAL, "variant = %d not 0 or 1", pr->variant);
     if (pr->n_nodes == 0 && pr->n_edges > 0) return fail(CTP_EGRAPH, "edges without nodes");
@@ -225,6 +225,8 @@ int32_t conv_tp_fwd(const conv_tp_problem* prob, const float* x, const float* y_
                     const int32_t* row_ptr, const int32_t* senders, float* out, void* stream) {
     Shape s{};
     if (int r = check_problem(prob, &s)) return r;
+    if (prob->algo == 2 && (prob->y_mode != 1 || prob->variant != ctp::kVariantSummed))
+        return fail(CTP_EUNSUPPORTED, "algo 2 (edge frame) needs edge vectors (y_mode 1) and variant 0");
     if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
     if (int r = need(y_or_vec, s.E * s.S, 4, "y_or_vec")) return r;
     if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;

@@ -1,0 +1,416 @@
+// Edge-aligned-frame forward of the convolution tensor product (gfx950), for
+// edge vectors (E2Former-V2, arXiv 2601.16622, abstract: equivariant products
+// sparsified by working in each edge's own frame, SO(2) style).
+//
+// For edge e with unit direction r, any rotation R with R r = z-hat gives,
+// with D^l = D^l(R) (Y_l(R v) = D^l Y_l(v)) and the coupling's equivariance
+// C_p(D1 a, D2 b) = D3 C_p(a, b):
+//
+//   C_p(x, Y(r)) = C_p(x, D^T Y(z-hat)) = D3^T C_p(D1 x, Y(z-hat)),
+//
+// and Y_l2(z-hat) is non-zero only at m2 = 0 (value sqrt((2 l2 + 1) / 4pi)).
+// So per edge and channel: x' = D x (84 FMA at l = 3), the m2 = 0 slice of
+// every path's coupling (111 non-zeros at l = 3) scaled by w, summed per l3 in
+// the frame, and one rotation back into the receiver's sum (84 FMA): about
+// 400 FMA instead of the direct form's 665, and 84 broadcast LDS values per
+// edge (D) instead of 541 (T).  The result equals the direct forward up to
+// rounding.
+//
+// D^l comes from the harmonics themselves: with seven fixed directions v_j,
+// M_l[a][j] = Y_la(v_j) has full row rank, so D^l = [Y_l(R v_j)]_j P_l with the
+// constant right inverse P_l = M_l^T (M_l M_l^T)^-1 (compile-time tables).
+// R is the shortest rotation taking r to z-hat (or to -z-hat followed by a
+// half turn about x when r_z < 0).  A zero edge vector has Y = (1/sqrt(4pi),
+// 0, ...): D = identity and the l2 >= 1 paths get weight 0.
+//
+// One workgroup per receiver and 64-channel tile, one channel per lane, edges
+// in CSR order with the same rotating prefetch as the direct forward; D of
+// the next edge is built into the other LDS buffer after each edge.  SPLIT
+// (small grids) halves each edge list as in the direct forward.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ctp {
+namespace {
+
+constexpr int kFrameThreads = 256;
+constexpr int kDirs = 7;                       // fixed directions v_j
+constexpr int kDOff[4] = {0, 0, 9, 34};        // D^l blocks (l >= 1) in the flat D table
+constexpr int kDEntries = 9 + 25 + 49;         // 83
+constexpr int kDPad = 84;
+
+// ------------------------------------------------------------ compile-time tables
+
+// Seven unit-ish directions (normalised below) whose harmonics have full rank
+// at l = 1, 2, 3 (condition numbers 2.2, 2.6, 2.8).
+constexpr double kDirRaw[kDirs][3] = {
+    {-0.8834895491600037, 0.03064717911183834, -0.46744731068611145},
+    {-0.6929545402526855, 0.7203747034072876, 0.02956932224333286},
+    {0.7007521390914917, 0.6210730671882629, 0.3510195314884186},
+    {0.9977782368659973, 0.04325412213802338, 0.05067275837063789},
+    {0.18411050736904144, -0.961883544921875, -0.20219644904136658},
+    {0.23605982959270477, -0.8178870677947998, 0.5247251391410828},
+    {-0.05702731758356094, -0.682953953742981, -0.7282319664955139},
+};
+
+// Real harmonic Y_{l,m} of a unit vector in double: the same recipe as the
+// device tables (A_m(x, y) * N_lm * d^|m|/dz^|m| P_l(z)).
+constexpr double sh_d(int l, int m, double x, double y, double z) {
+    double Pl[4][4] = {};
+    Pl[0][0] = 1.0;
+    Pl[1][1] = 1.0;
+    for (int n = 1; n < 3; ++n)
+        for (int d = 0; d < 4; ++d) {
+            double v = -n * Pl[n - 1][d];
+            if (d > 0) v += (2 * n + 1) * Pl[n][d - 1];
+            Pl[n + 1][d] = v / (n + 1);
+        }
+    const int a = m < 0 ? -m : m;
+    double poly[4] = {Pl[l][0], Pl[l][1], Pl[l][2], Pl[l][3]};
+    for (int r = 0; r < a; ++r)
+        for (int d = 0; d < 4; ++d) poly[d] = (d + 1 < 4) ? (d + 1) * poly[d + 1] : 0.0;
+    const double pi = 3.14159265358979323846;
+    double N = csqrt((2 * l + 1) / (4 * pi) * cfact(l - a) / cfact(l + a));
+    if (m != 0) N *= csqrt(2.0);
+    const double q = ((poly[3] * z + poly[2]) * z + poly[1]) * z + poly[0];
+    double re = 1.0, im = 0.0;
+    for (int k = 0; k < a; ++k) {
+        const double nr = re * x - im * y, ni = re * y + im * x;
+        re = nr;
+        im = ni;
+    }
+    return (m < 0 ? im : re) * N * q;
+}
+
+struct FrameTab {
+    float v[kDirs][3];                 // normalised directions
+    float p[kDirs][kDEntries];         // P_l[j][b] at p[j][kDOff[l] + b]
+};
+
+// P_l = M_l^T (M_l M_l^T)^-1, M_l[a][j] = Y_{l, a-l}(v_j); stored per l as
+// p[j][kDOff[l] + b], b < 2l+1 (the first 2l+1 slots of each block).
+constexpr FrameTab make_frame_tab() {
+    FrameTab t{};
+    double v[kDirs][3] = {};
+    for (int j = 0; j < kDirs; ++j) {
+        const double n = csqrt(kDirRaw[j][0] * kDirRaw[j][0] + kDirRaw[j][1] * kDirRaw[j][1] +
+                               kDirRaw[j][2] * kDirRaw[j][2]);
+        for (int c = 0; c < 3; ++c) {
+            v[j][c] = kDirRaw[j][c] / n;
+            t.v[j][c] = static_cast<float>(v[j][c]);
+        }
+    }
+    for (int l = 1; l <= 3; ++l) {
+        const int n = 2 * l + 1;
+        double M[7][kDirs] = {};
+        for (int a = 0; a < n; ++a)
+            for (int j = 0; j < kDirs; ++j) M[a][j] = sh_d(l, a - l, v[j][0], v[j][1], v[j][2]);
+        // G = M M^T, then its inverse by Gauss-Jordan with partial pivoting
+        double G[7][14] = {};
+        for (int a = 0; a < n; ++a) {
+            for (int b = 0; b < n; ++b) {
+                double s = 0.0;
+                for (int j = 0; j < kDirs; ++j) s += M[a][j] * M[b][j];
+                G[a][b] = s;
+            }
+            G[a][n + a] = 1.0;
+        }
+        for (int c = 0; c < n; ++c) {
+            int piv = c;
+            for (int r = c + 1; r < n; ++r)
+                if (cabs(G[r][c]) > cabs(G[piv][c])) piv = r;
+            for (int k = 0; k < 2 * n; ++k) {
+                const double tmp = G[c][k];
+                G[c][k] = G[piv][k];
+                G[piv][k] = tmp;
+            }
+            const double inv = 1.0 / G[c][c];
+            for (int k = 0; k < 2 * n; ++k) G[c][k] *= inv;
+            for (int r = 0; r < n; ++r)
+                if (r != c) {
+                    const double f = G[r][c];
+                    for (int k = 0; k < 2 * n; ++k) G[r][k] -= f * G[c][k];
+                }
+        }
+        for (int j = 0; j < kDirs; ++j)
+            for (int b = 0; b < n; ++b) {
+                double s = 0.0;
+                for (int a = 0; a < n; ++a) s += M[a][j] * G[a][n + b];
+                t.p[j][kDOff[l] + b] = static_cast<float>(s);
+            }
+    }
+    return t;
+}
+
+__constant__ FrameTab kFrameTab = make_frame_tab();
+__constant__ ShTab kFrameSh = make_sh_tab();   // this file's copy of the harmonic coefficients
+
+// Y_{l2,0}(z-hat) = sqrt((2 l2 + 1) / 4pi).
+constexpr float y_pole(int l2) {
+    const double pi = 3.14159265358979323846;
+    return static_cast<float>(csqrt((2 * l2 + 1) / (4 * pi)));
+}
+
+// One channel per lane: single-dword buffer accesses.
+__device__ __forceinline__ float ld1(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kCached));
+}
+__device__ __forceinline__ float ld1_stream(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream));
+}
+__device__ __forceinline__ void st1_stream(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, voff, soff, kStream);
+}
+
+// ------------------------------------------------------------ per-edge rotation D in LDS
+
+// The rotation taking the direction of v to z-hat (rows of R); false for a
+// zero vector.
+__device__ __forceinline__ bool frame_rotation(float vx, float vy, float vz, float (&R)[3][3]) {
+    const float n2 = vx * vx + vy * vy + vz * vz;
+    if (n2 == 0.0f) return false;
+    const float inv = 1.0f / sqrtf(n2);
+    float x = vx * inv, y = vy * inv, z = vz * inv;
+    const bool south = z < 0.0f;
+    if (south) {   // take -r to z-hat, then a half turn about x (diag(1, -1, -1))
+        x = -x;
+        y = -y;
+        z = -z;
+    }
+    const float k = 1.0f / (1.0f + z);   // z >= 0
+    R[0][0] = 1.0f - x * x * k;
+    R[0][1] = -x * y * k;
+    R[0][2] = -x;
+    R[1][0] = -x * y * k;
+    R[1][1] = 1.0f - y * y * k;
+    R[1][2] = -y;
+    R[2][0] = x;
+    R[2][1] = y;
+    R[2][2] = 1.0f - (x * x + y * y) * k;
+    if (south) {   // the half turn diag(1, -1, -1) after the map of -r to z-hat: R r = H (-z-hat) = z-hat
+        for (int c = 0; c < 3; ++c) {
+            R[1][c] = -R[1][c];
+            R[2][c] = -R[2][c];
+        }
+    }
+    return true;
+}
+
+// Builds D^1..D^3 of edge vector vp into sD (kDPad floats) in two lane-parallel
+// phases through sYR (P_l from its LDS copy sP); returns (uniformly) whether
+// the vector is non-zero.  Leaves the workgroup synchronised.
+template <int L>
+__device__ __forceinline__ bool build_frame(const float* __restrict__ vp, float* sD, float (*sYR)[16],
+                                            const float (*sP)[kDEntries], int tid, int nth) {
+    constexpr int D = (L + 1) * (L + 1);
+    float R[3][3];
+    const bool nonzero = frame_rotation(vp[0], vp[1], vp[2], R);
+    if (!nonzero) {   // no rotation: D = identity
+        for (int t = tid; t < kDOff[L] + (2 * L + 1) * (2 * L + 1) && L > 0; t += nth) {
+            const int l = t < 9 ? 1 : (t < 34 ? 2 : 3), n = 2 * l + 1, r = t - kDOff[l];
+            sD[t] = (r / n == r % n) ? 1.0f : 0.0f;
+        }
+    } else {
+        for (int t = tid; t < kDirs * D; t += nth) {
+            const int j = t / D, k = t - j * D;
+            const float* v = kFrameTab.v[j];
+            const float ux = R[0][0] * v[0] + R[0][1] * v[1] + R[0][2] * v[2];
+            const float uy = R[1][0] * v[0] + R[1][1] * v[1] + R[1][2] * v[2];
+            const float uz = R[2][0] * v[0] + R[2][1] * v[1] + R[2][2] * v[2];
+            sYR[j][k] = sh_component_c(k, kFrameSh.k[k], ux, uy, uz);
+        }
+        __syncthreads();
+        for (int t = tid; t < kDOff[L] + (2 * L + 1) * (2 * L + 1) && L > 0; t += nth) {
+            const int l = t < 9 ? 1 : (t < 34 ? 2 : 3), n = 2 * l + 1, r = t - kDOff[l];
+            const int a = r / n, b = r - a * n;
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kDirs; ++j) s = __builtin_fmaf(sYR[j][l * l + a], sP[j][kDOff[l] + b], s);
+            sD[t] = s;
+        }
+    }
+    __syncthreads();
+    return nonzero;
+}
+
+// ------------------------------------------------------------ forward kernel
+
+constexpr int dflat(int l, int a, int b) {
+    return kDOff[l] + a * (2 * l + 1) + b;
+}
+
+// One edge in its frame: x' = D x, m' = sum_p w_p * slice_p(x'), acc += D^T m';
+// the rows of the next edge are loaded into x and w as they are freed.
+template <int L, class S = Spec<L, L, L>>
+__device__ __forceinline__ void edge_frame(float (&acc)[S::D1], float (&xv)[S::D1], float (&wv)[S::P],
+                                           const float* sD, float f, rsrc_t nx, rsrc_t nw, uint32_t nvoff,
+                                           int C) {
+    constexpr int D = S::D1;
+    float xr[D];
+    xr[0] = xv[0];
+    static_for<L>([&](auto lI) __attribute__((always_inline)) {
+        constexpr int l = decltype(lI)::value + 1, n = 2 * l + 1, o = l * l;
+        static_for<n>([&](auto aI) __attribute__((always_inline)) {
+            constexpr int a = decltype(aI)::value;
+            float s = slot_value<dflat(l, a, 0)>(sD) * xv[o];
+            static_for<n - 1>([&](auto bI) __attribute__((always_inline)) {
+                constexpr int b = decltype(bI)::value + 1;
+                s = __builtin_fmaf(slot_value<dflat(l, a, b)>(sD), xv[o + b], s);
+            });
+            xr[o + a] = s;
+        });
+    });
+    // x is consumed: the next sender's row goes into its registers
+    {
+        const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+#pragma unroll
+        for (int d = 0; d < D; ++d) xv[d] = ld1(nx, nvoff, (uint32_t)d * c4);
+    }
+    float mr[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) mr[d] = 0.0f;
+    static_for<S::P>([&](auto pI) __attribute__((always_inline)) {
+        constexpr int p = decltype(pI)::value;
+        constexpr PathL q = S::paths[p];
+        constexpr int o1 = q.l1 * q.l1, o3 = q.l3 * q.l3;
+        constexpr float yz = y_pole(q.l2);
+        constexpr int n0 = nz_begin<S>(p), n1 = nz_begin<S>(p + 1);
+        // f = 0 drops the l2 >= 1 paths for a zero edge vector (Y = Y_00 only)
+        const float wp = q.l2 == 0 ? wv[p] : wv[p] * f;
+        static_for<n1 - n0>([&](auto zI) __attribute__((always_inline)) {
+            constexpr CgNz z = S::nz[n0 + decltype(zI)::value];
+            if constexpr (z.m2 == q.l2) {   // the m2 = 0 component of block l2
+                const float t = wp * xr[o1 + z.m1];
+                mr[o3 + z.m3] = __builtin_fmaf(z.c * yz, t, mr[o3 + z.m3]);
+            }
+        });
+        const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+        wv[p] = ld1_stream(nw, nvoff, (uint32_t)p * c4);
+        __builtin_amdgcn_sched_barrier(0x100);
+    });
+    // re-read D from LDS for the way back rather than keep the 84 values of the
+    // first rotation live in registers through the path loop
+    asm volatile("" ::: "memory");
+    acc[0] += mr[0];
+    static_for<L>([&](auto lI) __attribute__((always_inline)) {
+        constexpr int l = decltype(lI)::value + 1, n = 2 * l + 1, o = l * l;
+        static_for<n>([&](auto aI) __attribute__((always_inline)) {
+            constexpr int a = decltype(aI)::value;
+            static_for<n>([&](auto bI) __attribute__((always_inline)) {
+                constexpr int b = decltype(bI)::value;
+                acc[o + b] = __builtin_fmaf(slot_value<dflat(l, a, b)>(sD), mr[o + a], acc[o + b]);
+            });
+        });
+    });
+#pragma unroll
+    for (int d = 0; d < D; ++d) pin_f32(acc[d]);
+}
+
+template <int L, bool SPLIT>
+__global__ void __launch_bounds__(kFrameThreads)
+k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, const float* __restrict__ w,
+            const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ out) {
+    using S = Spec<L, L, L>;
+    constexpr int D = S::D1, P = S::P;
+    __shared__ __attribute__((aligned(16))) float sD[2][kDPad];
+    __shared__ float sYR[kDirs][16];
+    __shared__ float sP[kDirs][kDEntries];
+
+    const int i = blockIdx.x;
+    const int tid = threadIdx.x, nth = blockDim.x;
+    const int c0 = blockIdx.y * nth + tid;
+    const uint32_t voff = opaque_lane(c0 < C ? (uint32_t)c0 * 4u : kOffLane);
+
+    float acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = 0.0f;
+
+    int e0 = row_ptr[i], e1 = row_ptr[i + 1];
+    if constexpr (SPLIT) {
+        const int mid = e0 + (e1 - e0 + 1) / 2;
+        if (blockIdx.z == 0) e1 = mid; else e0 = mid;
+    }
+    if (e0 < e1) {
+        float xv[D], wv[P];
+        {
+            const long j = senders[e0];
+            const rsrc_t xr = make_row(x + j * D * C, (long)D * C);
+            const rsrc_t wr = make_row(w + (long)e0 * P * C, (long)P * C);
+            const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+#pragma unroll
+            for (int d = 0; d < D; ++d) xv[d] = ld1(xr, voff, (uint32_t)d * c4);
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                wv[p] = ld1_stream(wr, voff, (uint32_t)p * c4);
+        }
+        for (int t = tid; t < kDirs * kDEntries; t += nth) sP[t / kDEntries][t % kDEntries] = (&kFrameTab.p[0][0])[t];
+        bool nonzero = build_frame<L>(vec + 3L * e0, sD[0], sYR, sP, tid, nth);
+        for (int e = e0; e < e1; ++e) {
+            const int buf = (e - e0) & 1;
+            const bool has_next = e + 1 < e1;
+            const long en = has_next ? e + 1 : e;
+            const long jn = senders[en];
+            const rsrc_t nx = make_row(x + jn * D * C, (long)D * C);
+            const rsrc_t nw = make_row(w + en * P * C, (long)P * C);
+            const uint32_t nvoff = has_next ? voff : kOffLane;
+            edge_frame<L>(acc, xv, wv, sD[buf], nonzero ? 1.0f : 0.0f, nx, nw, nvoff, C);
+            if (has_next) nonzero = build_frame<L>(vec + 3 * en, sD[buf ^ 1], sYR, sP, tid, nth);
+        }
+    }
+    if constexpr (SPLIT) {
+        if (e0 < e1 && c0 < C) {
+            float* o = out + (long)i * D * C + c0;
+#pragma unroll
+            for (int d = 0; d < D; ++d) unsafeAtomicAdd(o + (long)d * C, acc[d]);
+        }
+    } else {
+        const rsrc_t orow = make_row(out + (long)i * D * C, (long)D * C);
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            st1_stream(orow, voff, (uint32_t)(d * C * 4), acc[d]);
+    }
+}
+
+__global__ void k_zero_frame(float* __restrict__ p, long n) {
+    long k = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (; k < n; k += stride) p[k] = 0.0f;
+}
+
+constexpr long kFrameSplitBelowWaves = 4L * 1024;
+
+template <int L>
+hipError_t frame_L(const LaunchArgs& a, hipStream_t st) {
+    const int waves_needed = (a.C + 63) / 64;
+    const int waves = waves_needed < kFrameThreads / 64 ? waves_needed : kFrameThreads / 64;
+    const int tiles = (waves_needed + waves - 1) / waves;
+    const bool split = (long)a.n_nodes * tiles * waves < kFrameSplitBelowWaves;
+    const dim3 block(64 * waves);
+    if (split) {
+        const long n = (long)a.n_nodes * (L + 1) * (L + 1) * a.C;
+        hipLaunchKernelGGL(k_zero_frame, dim3(1024), dim3(256), 0, st, a.out, n);
+        hipLaunchKernelGGL((k_fwd_frame<L, true>), dim3(a.n_nodes, tiles, 2), block, 0, st, a.C, a.x, a.y, a.w,
+                           a.row_ptr, a.senders, a.out);
+    } else {
+        hipLaunchKernelGGL((k_fwd_frame<L, false>), dim3(a.n_nodes, tiles), block, 0, st, a.C, a.x, a.y, a.w,
+                           a.row_ptr, a.senders, a.out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_frame(const LaunchArgs& a, hipStream_t st) {
+    if (a.n_nodes == 0) return hipSuccess;
+    switch (a.L) {
+        case 0: return frame_L<0>(a, st);
+        case 1: return frame_L<1>(a, st);
+        case 2: return frame_L<2>(a, st);
+        case 3: return frame_L<3>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ctp

@@ -1205,6 +1205,7 @@ bool bwd_supports_channels(int C) {
 
 hipError_t launch_fwd(const LaunchArgs& a, hipStream_t st) {
     if (a.n_nodes == 0) return hipSuccess;
+    if (a.algo == 2) return launch_fwd_frame(a, st);
     switch (a.L) {
         case 0: return fwd_L<0>(a, st);
         case 1: return fwd_L<1>(a, st);

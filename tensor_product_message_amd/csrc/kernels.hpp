@@ -10,7 +10,7 @@ namespace ctp {
 struct LaunchArgs {
     int L;                 // l_in = l_sh = l_out
     int n_nodes, n_edges, C;
-    int algo;              // 0: CSR deterministic, 1: edge-parallel atomic (forward only)
+    int algo;              // 0: CSR deterministic, 1: edge-parallel atomic, 2: edge frame (forward only)
     int vec_mode;          // 0: Y[E][D] given, 1: vec[E][3] given
     int variant;           // 0: all paths, same-l3 sums; 1: natural-parity paths, one output slot each
     const float* x;        // [N][D][C]
@@ -46,6 +46,8 @@ struct DoubleArgs {
 hipError_t launch_fwd(const LaunchArgs& a, hipStream_t st);
 hipError_t launch_double_bwd(const DoubleArgs& a, hipStream_t st);
 bool dd_supports_channels(int C);
+// Forward in each edge's own frame (edge vectors, summed variant).
+hipError_t launch_fwd_frame(const LaunchArgs& a, hipStream_t st);
 hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st);
 // Backward through an edge-message workspace msg[E][D][C]: receiver-major
 // products, then per-sender sums of the messages.

@@ -23,7 +23,7 @@ from . import _capi
 from ._capi import ConvTPError, Problem, check, lib  # noqa: F401
 
 Y_GIVEN, VEC_GIVEN = 0, 1
-ALGO_CSR, ALGO_ATOMIC = 0, 1
+ALGO_CSR, ALGO_ATOMIC, ALGO_FRAME = 0, 1, 2   # ALGO_FRAME: edge-frame forward (edge vectors)
 SUMMED, SLOTS = 0, 1          # path variants (conv_tp_problem.variant)
 
 

@@ -116,6 +116,16 @@ def test_fwd_rejects_bad_pointers(capi):
     assert "aligned" in capi.lib().conv_tp_last_error().decode()
 
 
+def test_frame_forward_rejections(capi):
+    # the edge-frame forward (algo 2) needs edge vectors and the summed variant
+    assert _fwd(capi, _prob(capi, algo=2, y_mode=0)) == capi.CTP_EUNSUPPORTED
+    assert _fwd(capi, _prob(capi, algo=2, y_mode=1, variant=1)) == capi.CTP_EUNSUPPORTED
+    assert "edge frame" in capi.lib().conv_tp_last_error().decode()
+    assert _fwd(capi, _prob(capi, algo=3, y_mode=1)) == capi.CTP_EINVAL
+    assert _fwd(capi, _prob(capi, algo=2, y_mode=1), x=NUL) == capi.CTP_EINVAL
+    assert _bwd(capi, _prob(capi, algo=2, y_mode=1)) == capi.CTP_EUNSUPPORTED
+
+
 def test_bwd_rejections(capi):
     assert _bwd(capi, _prob(capi, algo=1)) == capi.CTP_EUNSUPPORTED
     assert _bwd(capi, _prob(capi, channels=1024)) == capi.CTP_EUNSUPPORTED

@@ -542,6 +542,72 @@ def test_variant_slots_full_l3_sampled(ctp, dev):
     close("dY[sample]", host(dy[ei]), dY_ref)
 
 
+# ------------------------------------------------------------ forward in each edge's frame (algo 2)
+
+
+@pytest.mark.parametrize("n,c,L", SMALL)
+def test_frame_forward_small(ctp, dev, n, c, L):
+    d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=n + c + L + 5)
+    run_small(ctp, dev, d, L, 1, ctp.ALGO_FRAME, bwd=False)
+
+
+def test_frame_forward_poles_zero_vectors_and_hub(ctp, dev):
+    """Edge vectors along +z and -z (exact and within 1e-7 of them), zero
+    vectors, a 1000-in-degree hub, self and duplicate edges."""
+    rng = np.random.default_rng(44)
+    n, c, L = 40, 96, 3
+    recv = np.sort(np.concatenate([np.full(1000, 3), rng.integers(0, n, size=300)]))
+    s = rng.integers(0, n, size=recv.size)
+    s[:10] = recv[:10]
+    e = recv.size
+    vec = rng.standard_normal((e, 3)).astype(np.float32)
+    vec[::37] = 0.0
+    vec[1::41] = (0.0, 0.0, 2.5)
+    vec[2::41] = (0.0, 0.0, -0.5)
+    vec[3::41] = (1e-7, -1e-7, -1.0)
+    vec[4::41] = (-1e-7, 0.0, 1.0)
+    vec[5::41] = (1.0, 0.0, 0.0)
+    d = dict(n_nodes=n, n_edges=e, row_ptr=og.row_ptr_from_receivers(recv, n), senders=s.astype(np.int32), vec=vec,
+             x=rng.standard_normal((n, 16, c)).astype(np.float32),
+             w=rng.standard_normal((e, 34, c)).astype(np.float32))
+    run_small(ctp, dev, d, L, 1, ctp.ALGO_FRAME, bwd=False)
+
+
+def test_frame_forward_full_l3_sampled_and_deterministic(ctp, dev):
+    """lmax=3, N=16384, C=128, Poisson(45), edge vectors: sampled receivers
+    against the oracle, the whole output against the direct forward, and
+    bitwise equal reruns."""
+    n, c, L = 16384, 128, 3
+    d = gen.poisson_full(n, c, L, dev, seed=2, need_grad=False)
+    rp, s, vec = d["row_ptr"], d["senders"], d["vec"]
+    g = ctp.Graph(n, T(rp, dev), T(s, dev))
+    v = T(vec, dev)
+    print("frame forward full l3", flush=True)
+    out = ctp.conv_tp_fwd(d["x"], v, d["w"], g, L, 1, ctp.ALGO_FRAME)
+    again = ctp.conv_tp_fwd(d["x"], v, d["w"], g, L, 1, ctp.ALGO_FRAME)
+    assert torch.equal(out, again)
+    direct = ctp.conv_tp_fwd(d["x"], v, d["w"], g, L, 1, ctp.ALGO_CSR)
+    close("out vs direct forward", host(out), host(direct))
+    rng = np.random.default_rng(9)
+    rows = np.sort(rng.choice(n, 32, replace=False))
+    close("out[sample]", host(out[torch.as_tensor(rows, device=dev)]),
+          _sub_fwd(oc.Problem(L, L, L), rp, s, osh.real_sh(L, vec.astype(np.float64)), d["w"], host(d["x"]), rows))
+
+
+def test_frame_forward_water_box(ctp, dev):
+    """The water box (1503 receivers: the small-grid split) with edge vectors."""
+    wb = gen.water_box(seed=0, device="cpu")
+    n, L = wb["n_nodes"], 3
+    g = ctp.Graph(n, T(wb["row_ptr"], dev), T(wb["senders"], dev))
+    w1 = wb["w1"].numpy()
+    x, v, w = T(wb["x"], dev), T(wb["vec"], dev), T(w1, dev)
+    print("frame forward water box", flush=True)
+    out = ctp.conv_tp_fwd(x, v, w, g, L, 1, ctp.ALGO_FRAME)
+    ref = oc.fwd(oc.Problem(L, L, L), wb["x"], osh.real_sh(L, wb["vec"].astype(np.float64)), w1,
+                 wb["row_ptr"], wb["senders"])
+    close("out", host(out), ref)
+
+
 # ------------------------------------------------------------ backward through edge messages
 
 
