@@ -199,11 +199,14 @@ __device__ __forceinline__ bool frame_rotation(float vx, float vy, float vz, flo
 }
 
 // Builds D^1..D^3 of edge vector vp into sD (kDPad floats) in two lane-parallel
-// phases through sYR (P_l from its LDS copy sP); returns (uniformly) whether
-// the vector is non-zero.  Leaves the workgroup synchronised.
+// phases through sYR (directions, harmonic coefficients and P_l from their
+// LDS copies: no global loads on the per-edge path); returns (uniformly)
+// whether the vector is non-zero.  Leaves the workgroup synchronised.  (Moving
+// the first phase ahead of the previous edge's arithmetic measured no faster.)
 template <int L>
 __device__ __forceinline__ bool build_frame(const float* __restrict__ vp, float* sD, float (*sYR)[16],
-                                            const float (*sP)[kDEntries], int tid, int nth) {
+                                            const float (*sP)[kDEntries], const float (*sV)[3], const ShCoef* sSh,
+                                            int tid, int nth) {
     constexpr int D = (L + 1) * (L + 1);
     float R[3][3];
     const bool nonzero = frame_rotation(vp[0], vp[1], vp[2], R);
@@ -215,11 +218,11 @@ __device__ __forceinline__ bool build_frame(const float* __restrict__ vp, float*
     } else {
         for (int t = tid; t < kDirs * D; t += nth) {
             const int j = t / D, k = t - j * D;
-            const float* v = kFrameTab.v[j];
+            const float* v = sV[j];
             const float ux = R[0][0] * v[0] + R[0][1] * v[1] + R[0][2] * v[2];
             const float uy = R[1][0] * v[0] + R[1][1] * v[1] + R[1][2] * v[2];
             const float uz = R[2][0] * v[0] + R[2][1] * v[1] + R[2][2] * v[2];
-            sYR[j][k] = sh_component_c(k, kFrameSh.k[k], ux, uy, uz);
+            sYR[j][k] = sh_component_c(k, sSh[k], ux, uy, uz);
         }
         __syncthreads();
         for (int t = tid; t < kDOff[L] + (2 * L + 1) * (2 * L + 1) && L > 0; t += nth) {
@@ -317,6 +320,8 @@ k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, c
     __shared__ __attribute__((aligned(16))) float sD[2][kDPad];
     __shared__ float sYR[kDirs][16];
     __shared__ float sP[kDirs][kDEntries];
+    __shared__ float sV[kDirs][3];
+    __shared__ ShCoef sSh[16];
 
     const int i = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
@@ -345,8 +350,12 @@ k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, c
             for (int p = 0; p < P; ++p)
                 wv[p] = ld1_stream(wr, voff, (uint32_t)p * c4);
         }
+        // per-edge constants into LDS once: P_l, the directions, the harmonic coefficients
         for (int t = tid; t < kDirs * kDEntries; t += nth) sP[t / kDEntries][t % kDEntries] = (&kFrameTab.p[0][0])[t];
-        bool nonzero = build_frame<L>(vec + 3L * e0, sD[0], sYR, sP, tid, nth);
+        if (tid < kDirs * 3) sV[tid / 3][tid % 3] = kFrameTab.v[tid / 3][tid % 3];
+        if (tid < 16) sSh[tid] = kFrameSh.k[tid];
+        __syncthreads();
+        bool nonzero = build_frame<L>(vec + 3L * e0, sD[0], sYR, sP, sV, sSh, tid, nth);
         for (int e = e0; e < e1; ++e) {
             const int buf = (e - e0) & 1;
             const bool has_next = e + 1 < e1;
@@ -356,7 +365,7 @@ k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, c
             const rsrc_t nw = make_row(w + en * P * C, (long)P * C);
             const uint32_t nvoff = has_next ? voff : kOffLane;
             edge_frame<L>(acc, xv, wv, sD[buf], nonzero ? 1.0f : 0.0f, nx, nw, nvoff, C);
-            if (has_next) nonzero = build_frame<L>(vec + 3 * en, sD[buf ^ 1], sYR, sP, tid, nth);
+            if (has_next) nonzero = build_frame<L>(vec + 3 * en, sD[buf ^ 1], sYR, sP, sV, sSh, tid, nth);
         }
     }
     if constexpr (SPLIT) {
