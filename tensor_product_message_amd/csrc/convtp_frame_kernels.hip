@@ -23,10 +23,10 @@
 // half turn about x when r_z < 0).  A zero edge vector has Y = (1/sqrt(4pi),
 // 0, ...): D = identity and the l2 >= 1 paths get weight 0.
 //
-// One workgroup per receiver and 64-channel tile, one channel per lane, edges
-// in CSR order with the same rotating prefetch as the direct forward; D of
-// the next edge is built into the other LDS buffer after each edge.  SPLIT
-// (small grids) halves each edge list as in the direct forward.
+// One workgroup per receiver and channel tile (up to four waves), one channel
+// per lane, edges in CSR order with the same rotating prefetch as the direct
+// forward; D of the next edge is built into the other LDS buffer after each
+// edge.  SPLIT (small grids) halves each edge list as in the direct forward.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -382,6 +382,9 @@ k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, c
     }
 }
 
+// Zero fill before the split's atomics (a kernel, not a memset, so that the
+// call can be captured in a HIP graph; the library's other fill lives in
+// another translation unit).
 __global__ void k_zero_frame(float* __restrict__ p, long n) {
     long k = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const long stride = (long)gridDim.x * blockDim.x;
