@@ -271,7 +271,7 @@ int32_t conv_tp_stream_probe(int32_t kind, const float *src, float *dst, int64_t
 const char *conv_tp_last_error(void);
 
 /* ABI version (major * 100 + minor): 101 added conv_tp_problem.variant, 102
- * conv_tp_bwd_msg. */
+ * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward). */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

@@ -178,7 +178,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 102; }
+int32_t conv_tp_version(void) { return 103; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
