@@ -248,7 +248,7 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
                     constexpr int l3 = decltype(l3I)::value;
                     constexpr PairPaths pp = pair_paths<S>(l1, l3);
                     if constexpr (pp.n > 0) {
-                        constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
+                        constexpr int n1 = 2 * l1 + 1;
                         constexpr int o1 = l1 * l1, o3 = l3 * l3;
                         // (a) v, v', gw and gx for the pair's paths
                         static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
