@@ -180,6 +180,32 @@ def workload_l3dd(ctp, torch, dev, args):
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="dd", edges=e, cfg=cfg, cpu=None, bound="alu")
 
 
+def workload_l3ddvec(ctp, torch, dev, args):
+    """VJP of the edge-vector backward at lmax=3, N=16384, C=128, Poisson(45):
+    the gradients of <ax, dx> + <aw, dw> + <avec, dvec> in x, w, vec and G, by
+    the library calls ops.conv_tp_bwd_bwd_vec chains (harmonics, dY alone,
+    harmonic JVP, the double backward, harmonic second-order term)."""
+    from workloads import gen
+    L = 3
+    d, g, vec = make_poisson(ctp, torch, dev, 16384, 128, L, ctp.VEC_GIVEN, True)
+    ax, aw, _ = gen.cotangents_full(d, dev, seed=0)
+    avec = torch.randn(vec.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev)
+    x, w, G = d["x"], d["w"], d["grad_out"]
+    n, e, c = 16384, d["n_edges"], 128
+    D, P = (L + 1) ** 2, ctp.num_paths(L)
+
+    def step(t):
+        t.run("ddvec", lambda: ctp.conv_tp_bwd_bwd_vec(G, x, vec, w, ax, aw, avec, g, L))
+
+    # inputs read once and outputs written once: x, ax, G, w, aw, vec, avec and the
+    # graph arrays; gx, gG, gw, gvec
+    kb = {"ddvec": 4 * (3 * e * P * c + 4 * e * 3 + 4 * e + 2 * (n + 1) + 5 * n * D * c)}
+    cfg = {"workload": f"lmax=3 conv TP VJP-of-VJP with edge vectors, N=16384, C=128, E={e}, Poisson(45) "
+                       "in-degree, fp32",
+           "n_nodes": n, "n_edges": e, "channels": c, "lmax": L, "paths": P}
+    return dict(step=step, kernel_bytes=kb, dominant="ddvec", edges=e, cfg=cfg, cpu=None)
+
+
 def workload_l3mace(ctp, torch, dev, args):
     """MACE variant at lmax=3, N=16384, C=128, Poisson(45), Y given: natural-parity
     paths (P=23), one output slot per path (99 components per channel)."""
@@ -427,7 +453,7 @@ def workload_hbm(ctp, torch, dev, args):
 WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
              "water": workload_water, "tiny": workload_tiny, "copy": workload_copy, "hbm": workload_hbm,
              "node3": workload_node, "l3dd": workload_l3dd, "l3mace": workload_l3mace,
-             "gather": workload_gather}
+             "gather": workload_gather, "l3ddvec": workload_l3ddvec}
 
 
 # ------------------------------------------------------------ CPU baseline (oracle)

@@ -146,6 +146,18 @@ int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const fl
                     const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec,
                     void *stream);
 
+/* The harmonic gradient alone: dY[e, l2 m2] = sum_c sum_p w[e,p,c]
+ * sum_{m1,m3} C_p[m1][m2][m3] x[j, l1 m1, c] grad_out[i, l3 m3, c] (the dY of
+ * conv_tp_bwd, FlashCart's symbolic-VJP section), without dx and dw.  It does
+ * not depend on Y, so Y is not an argument.  dy (device, [E][D_sh]) is
+ * overwritten; one workgroup per receiver keeps grad_out's row in registers
+ * and sums over channels in a fixed order: bitwise equal to conv_tp_bwd's dY.
+ * For recomputing dY where dx and dw are not needed (the edge-vector VJP of
+ * the VJP).  y_mode must be 0, algo 0, C <= 512 (CTP_EUNSUPPORTED otherwise);
+ * both variants. */
+int32_t conv_tp_bwd_dy(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *w,
+                       const int32_t *row_ptr, const int32_t *senders, float *dy, void *stream);
+
 /* Bytes of device workspace conv_tp_bwd_msg needs: E * D_in * C * 4 with
  * D_in = (l_in+1)^2.  Pure host function; errors as conv_tp_bwd's problem
  * checks, CTP_EINVAL for a null bytes pointer. */
@@ -271,7 +283,7 @@ int32_t conv_tp_stream_probe(int32_t kind, const float *src, float *dst, int64_t
 const char *conv_tp_last_error(void);
 
 /* ABI version (major * 100 + minor): 101 added conv_tp_problem.variant, 102
- * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward). */
+ * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward), 104 conv_tp_bwd_dy. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

@@ -15,7 +15,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libconvtp.so")
-SOURCES = ["convtp_kernels.hip", "convtp_frame_kernels.hip", "convtp_dd_kernels.hip", "nodetp_kernels.hip", "graph_kernels.hip", "stream_probe.hip", "convtp_api.hip"]
+SOURCES = ["convtp_kernels.hip", "convtp_frame_kernels.hip", "convtp_dy_kernels.hip", "convtp_dd_kernels.hip", "nodetp_kernels.hip", "graph_kernels.hip", "stream_probe.hip", "convtp_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",

@@ -178,7 +178,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 103; }
+int32_t conv_tp_version(void) { return 104; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
@@ -254,6 +254,30 @@ int32_t conv_tp_bwd(const conv_tp_problem* prob, const float* grad_out, const fl
                          dy_or_dvec, &s, &a))
         return r;
     return hip_status(ctp::launch_bwd(a, static_cast<hipStream_t>(stream)), "conv_tp_bwd launch");
+}
+
+int32_t conv_tp_bwd_dy(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* w,
+                       const int32_t* row_ptr, const int32_t* senders, float* dy, void* stream) {
+    Shape s{};
+    if (int r = check_problem(prob, &s)) return r;
+    if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_dy has only the deterministic algorithm (algo 0)");
+    if (prob->y_mode != 0) return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_dy writes dY: y_mode must be 0");
+    if (!ctp::dy_supports_channels(prob->channels))
+        return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_dy needs C <= 512, got %d", prob->channels);
+    if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
+    if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
+    if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;
+    if (int r = need(row_ptr, s.N + 1, 4, "row_ptr")) return r;
+    if (int r = need(senders, s.E, 4, "senders")) return r;
+    if (int r = need(dy, s.E * s.D2, 4, "dy")) return r;
+    ctp::LaunchArgs a = base_args(prob);
+    a.grad = grad_out;
+    a.x = x;
+    a.w = w;
+    a.row_ptr = row_ptr;
+    a.senders = senders;
+    a.dy = dy;
+    return hip_status(ctp::launch_bwd_dy(a, static_cast<hipStream_t>(stream)), "conv_tp_bwd_dy launch");
 }
 
 int32_t conv_tp_bwd_msg_workspace(const conv_tp_problem* prob, int64_t* bytes) {

@@ -48,6 +48,9 @@ hipError_t launch_double_bwd(const DoubleArgs& a, hipStream_t st);
 bool dd_supports_channels(int C);
 // Forward in each edge's own frame (edge vectors, summed variant).
 hipError_t launch_fwd_frame(const LaunchArgs& a, hipStream_t st);
+// Harmonic gradient dY alone (Y given): receiver-major, G row once per receiver.
+hipError_t launch_bwd_dy(const LaunchArgs& a, hipStream_t st);
+bool dy_supports_channels(int C);
 hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st);
 // Backward through an edge-message workspace msg[E][D][C]: receiver-major
 // products, then per-sender sums of the messages.

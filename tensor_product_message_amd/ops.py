@@ -191,6 +191,22 @@ def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int =
     return dx, dw, dy
 
 
+def conv_tp_bwd_dy(grad_out, x, w, graph: Graph, lmax: int, dy=None, variant: int = SUMMED):
+    """dY alone (Y given): the harmonic gradient of conv_tp_bwd without dx and dw."""
+    n, e, c = x.shape[0], w.shape[0], x.shape[2]
+    if graph.n_nodes != n or graph.senders.numel() != e:
+        raise ValueError("graph does not match x / w")
+    _want(x, "x", (n, dim(lmax), c))
+    _want(w, "w", (e, len(layout(lmax, variant)[0]), c), device=x.device)
+    _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
+    dy = torch.empty((e, dim(lmax)), dtype=torch.float32, device=x.device) if dy is None else dy
+    _want(dy, "dy", (e, dim(lmax)), device=x.device)
+    prob = _problem(n, e, c, lmax, Y_GIVEN, ALGO_CSR, variant)
+    check(lib().conv_tp_bwd_dy(ctypes.byref(prob), _p(grad_out), _p(x), _p(w), _p(graph.row_ptr),
+                               _p(graph.senders), _p(dy), _stream(x)))
+    return dy
+
+
 def conv_tp_bwd_msg_workspace(n_nodes: int, n_edges: int, channels: int, lmax: int, y_mode: int = Y_GIVEN,
                               variant: int = SUMMED) -> int:
     """Bytes of device workspace conv_tp_bwd_msg needs (E * (lmax+1)^2 * C * 4)."""
@@ -340,10 +356,10 @@ def spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, lmax: int, out=None):
 def conv_tp_bwd_bwd_vec(grad_out, x, vec, w, a_x, a_w, a_vec, graph: Graph, lmax: int):
     """VJP of the edge-vector backward: (g_x, g_w, g_vec, g_grad) for
     cotangents (a_x, a_w, a_vec) of (dx, dw, dvec), by the library calls
-    include/convtp.h lists (harmonics, first backward with Y given for dY,
-    harmonic JVP, the double backward, and the harmonic second-order term)."""
+    include/convtp.h lists (harmonics, the first backward's dY alone, harmonic
+    JVP, the double backward, and the harmonic second-order term)."""
     Y = spherical_harmonics(vec, lmax)
-    _, _, dY = conv_tp_bwd(grad_out, x, Y, w, graph, lmax, Y_GIVEN)
+    dY = conv_tp_bwd_dy(grad_out, x, w, graph, lmax)
     a_y = spherical_harmonics_jvp(vec, a_vec, lmax)
     g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph, lmax)
     g_vec = spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, lmax)

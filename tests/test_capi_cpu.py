@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 103
+    assert L.conv_tp_version() == 104
 
 
 def test_paths_match_oracle(capi):
@@ -160,6 +160,23 @@ def test_bwd_msg_rejections(capi):
     assert "workspace" in L.conv_tp_last_error().decode()
     assert _bwd_msg(capi, p, ws=NUL, nbytes=nb.value) == capi.CTP_EINVAL
     assert _bwd_msg(capi, p, ws=MIS, nbytes=nb.value) == capi.CTP_EALIGN
+
+
+def test_bwd_dy_rejections(capi):
+    L = capi.lib()
+    f = lambda p, a: L.conv_tp_bwd_dy(ctypes.byref(p), *a, NUL)  # noqa: E731
+    args = [A, A, A, A, A, A2]          # grad_out, x, w, row_ptr, senders, dy
+    assert len(L.conv_tp_bwd_dy.argtypes) == 8
+    assert f(_prob(capi, y_mode=1), args) == capi.CTP_EUNSUPPORTED
+    assert f(_prob(capi, algo=1), args) == capi.CTP_EUNSUPPORTED
+    assert f(_prob(capi, channels=513), args) == capi.CTP_EUNSUPPORTED
+    for k in range(6):
+        a = list(args)
+        a[k] = NUL
+        assert f(_prob(capi), a) == capi.CTP_EINVAL, k
+    a = list(args)
+    a[1] = MIS
+    assert f(_prob(capi), a) == capi.CTP_EALIGN
 
 
 def test_node_entry_points_validate(capi):

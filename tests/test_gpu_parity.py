@@ -542,6 +542,55 @@ def test_variant_slots_full_l3_sampled(ctp, dev):
     close("dY[sample]", host(dy[ei]), dY_ref)
 
 
+# ------------------------------------------------------------ harmonic gradient alone
+
+
+@pytest.mark.parametrize("n,c,L", [(90, 16, 1), (150, 48, 2), (100, 128, 3), (60, 192, 3), (40, 96, 0),
+                                   (30, 512, 2), (50, 7, 2)])
+@pytest.mark.parametrize("variant", [0, 1])
+def test_bwd_dy_small(ctp, dev, n, c, L, variant):
+    """conv_tp_bwd_dy against the oracle's dY and bitwise against conv_tp_bwd's."""
+    d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=n + c + L + 9)
+    if variant == 1:
+        d = _variant_inputs(d, L)
+    prob = oc.Problem(L, L, L, variant=variant)
+    Y = sh32(L, d["vec"])
+    g = ctp.Graph(d["n_nodes"], T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w, G = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev)
+    print(f"bwd_dy n={n} c={c} L={L} variant={variant}", flush=True)
+    dy = ctp.conv_tp_bwd_dy(G, x, w, g, L, variant=variant)
+    _, dY_ref = oc.bwd_edges(prob, d["x"], Y.astype(np.float64), d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+    close("dY", host(dy), dY_ref)
+    _, _, dy0 = ctp.conv_tp_bwd(G, x, T(Y, dev), w, g, L, 0, variant=variant)
+    assert torch.equal(dy, dy0)
+
+
+def test_bwd_dy_full_l3_and_isolated_receivers(ctp, dev):
+    """lmax=3, N=16384, C=128: bitwise equal to the full backward's dY; and a
+    graph with receivers that have no in-edges."""
+    n, c, L = 16384, 128, 3
+    d = gen.poisson_full(n, c, L, dev, seed=4, need_grad=True)
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    Y = T(sh32(L, d["vec"]), dev)
+    print("bwd_dy full l3", flush=True)
+    dy = ctp.conv_tp_bwd_dy(d["grad_out"], d["x"], d["w"], g, L)
+    _, _, dy0 = ctp.conv_tp_bwd(d["grad_out"], d["x"], Y, d["w"], g, L, 0)
+    assert torch.equal(dy, dy0)
+    rng = np.random.default_rng(3)
+    recv = np.sort(rng.integers(0, 10, size=200))        # receivers 10..39 have no in-edges
+    dd = dict(n_nodes=40, n_edges=200, row_ptr=og.row_ptr_from_receivers(recv, 40),
+              senders=rng.integers(0, 40, size=200).astype(np.int32),
+              vec=rng.standard_normal((200, 3)).astype(np.float32),
+              x=rng.standard_normal((40, 16, 64)).astype(np.float32),
+              w=rng.standard_normal((200, 34, 64)).astype(np.float32),
+              grad_out=rng.standard_normal((40, 16, 64)).astype(np.float32))
+    g2 = ctp.Graph(40, T(dd["row_ptr"], dev), T(dd["senders"], dev))
+    dy2 = ctp.conv_tp_bwd_dy(T(dd["grad_out"], dev), T(dd["x"], dev), T(dd["w"], dev), g2, L)
+    _, ref = oc.bwd_edges(oc.Problem(L, L, L), dd["x"], sh32(L, dd["vec"]).astype(np.float64), dd["w"],
+                          dd["grad_out"], dd["row_ptr"], dd["senders"])
+    close("dY", host(dy2), ref)
+
+
 # ------------------------------------------------------------ forward in each edge's frame (algo 2)
 
 
