@@ -1,5 +1,5 @@
 """The library driven from plain C: tests/c_abi/roundtrip (a C99 program
-built by __graft_entry__.build() or `python tests/c_abi/build.py`) allocates
+built by the repository build entry point or `python tests/c_abi/build.py`) allocates
 device memory with the HIP runtime, builds the transpose and runs the
 forward and a backward through include/convtp.h; its outputs are compared
 with the oracle (transpose arrays bit-exact)."""
