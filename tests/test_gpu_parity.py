@@ -193,6 +193,88 @@ def test_hip_graph_replays(ctp, dev, n, c):
             assert torch.equal(a, b), (k, name)
 
 
+def test_hip_graph_replays_frame_and_dy(ctp, dev):
+    """The edge-frame forward (small-grid split: its zero fill is a kernel) and
+    dY alone, captured in a HIP graph and replayed with eager work between."""
+    L, n, c = 3, 300, 128
+    d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=77)
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w, G, v = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev), T(d["vec"], dev)
+    out, dy = torch.empty_like(x), torch.empty(d["n_edges"], 16, device=dev)
+
+    def run():
+        ctp.conv_tp_fwd(x, v, w, g, L, 1, ctp.ALGO_FRAME, out=out)
+        ctp.conv_tp_bwd_dy(G, x, w, g, L, dy=dy)
+
+    print("graph capture frame + dy", flush=True)
+    run()
+    torch.cuda.synchronize()
+    ref = (out.clone(), dy.clone())
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for k in range(3):
+        out.fill_(float("nan"))
+        dy.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(dy, ref[1]), k
+
+
+def test_random_shapes_every_entry_point(ctp, dev):
+    """Seeded random problems (degree, channel count including ragged ones,
+    graph size with empty rows, both Y modes, both variants) through every
+    conv entry point: forward algos 0/1/2, backward, message backward and dY
+    alone, each against the oracle."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        L = int(rng.integers(0, 4))
+        c = int(rng.choice([1, 3, 17, 64, 65, 100, 128, 129, 200, 256, 300]))
+        n = int(rng.integers(2, 60))
+        e = int(rng.integers(0, 4 * n))
+        variant = int(rng.integers(0, 2))
+        y_mode = int(rng.integers(0, 2))
+        recv = np.sort(rng.integers(0, n, size=e))
+        pr = oc.Problem(L, L, L, variant=variant)
+        d = dict(n_nodes=n, n_edges=e, row_ptr=og.row_ptr_from_receivers(recv, n),
+                 senders=rng.integers(0, n, size=e).astype(np.int32),
+                 vec=rng.standard_normal((e, 3)).astype(np.float32),
+                 x=rng.standard_normal((n, pr.D1, c)).astype(np.float32),
+                 w=rng.standard_normal((e, pr.P, c)).astype(np.float32),
+                 grad_out=rng.standard_normal((n, pr.D3, c)).astype(np.float32))
+        print(f"case {case}: L={L} c={c} n={n} e={e} variant={variant} y_mode={y_mode}", flush=True)
+        Y = sh32(L, d["vec"])
+        yin = Y if y_mode == 0 else d["vec"]
+        Yref = Y.astype(np.float64) if y_mode == 0 else osh.real_sh(L, d["vec"].astype(np.float64))
+        g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+        x, w, G, yv = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev), T(yin, dev)
+        nz = e > 0
+        ref = oc.fwd(pr, d["x"], Yref, d["w"], d["row_ptr"], d["senders"])
+        algos = [0, 1] + ([2] if y_mode == 1 and variant == 0 else [])
+        for algo in algos:
+            close(f"out algo {algo}", host(ctp.conv_tp_fwd(x, yv, w, g, L, y_mode, algo, variant=variant)), ref,
+                  nonzero=nz)
+        if c > 512:
+            continue
+        sp, pe, sr = og.transpose(n, d["row_ptr"], d["senders"])
+        dx_ref = oc.bwd_dx(pr, Yref, d["w"], d["grad_out"], sp, pe, sr)
+        dw_ref, dY_ref = oc.bwd_edges(pr, d["x"], Yref, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+        dy_ref = dY_ref if y_mode == 0 else osh.vec_grad_from_sh_grad(L, d["vec"].astype(np.float64), dY_ref)
+        for name, fn in (("bwd", ctp.conv_tp_bwd), ("bwd_msg", ctp.conv_tp_bwd_msg)):
+            dx, dw, dy = fn(G, x, yv, w, g, L, y_mode, variant=variant)
+            close(f"{name} dx", host(dx), dx_ref, nonzero=nz)
+            close(f"{name} dw", host(dw), dw_ref, nonzero=nz)
+            close(f"{name} dy", host(dy), dy_ref, nonzero=nz and (y_mode == 0 or L > 0))
+        if y_mode == 0:
+            close("dY alone", host(ctp.conv_tp_bwd_dy(G, x, w, g, L, variant=variant)), dY_ref, nonzero=nz)
+
+
 # ------------------------------------------------------------ bookkeeping and harmonics
 
 
