@@ -43,19 +43,35 @@ def bwd_bytes(N, E, C, D1, D2, D3, P, S):
     return 4 * (2 * E * P * C + 2 * E * S + 2 * E + (N + 1) + 2 * N * C * D1 + N * C * D3)
 
 
-KERNEL_HEADERS = ("device_common.hpp", "tables.hpp", "kernels.hpp")
-# the source each workload's kernels are compiled from (besides the headers)
-WORKLOAD_SOURCE = {"node3": "nodetp_kernels.hip", "l3dd": "convtp_dd_kernels.hip", "hbm": "stream_probe.hip"}
+# every source a workload's kernels are compiled or dispatched from
+COMMON_SOURCES = ("device_common.hpp", "tables.hpp", "kernels.hpp", "convtp_api.hip")
+CONV_SOURCES = ("convtp_triple.hip", "convtp_common.hip", "conv_fwd.hpp", "conv_bwd.hpp", "conv_dy.hpp",
+                "conv_dd.hpp", "conv_frame.hpp")
+WORKLOAD_SOURCES = {"node3": ("nodetp_kernels.hip",), "hbm": ("stream_probe.hip",)}
 
 
 def kernel_sources_sha(workload="l3fb"):
-    """Hash of the sources the workload's kernels are compiled from."""
+    """Hash of every source the workload's kernels are compiled or dispatched from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_product_message_amd", "csrc")
-    for f in (WORKLOAD_SOURCE.get(workload, "convtp_kernels.hip"),) + KERNEL_HEADERS:
+    for f in WORKLOAD_SOURCES.get(workload.split("-")[0], CONV_SOURCES) + COMMON_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def run_tag(args):
+    """Name of what a run measures: the workload plus the options that change
+    which kernels run (edge vectors, edge-frame forward, sender-major MACE
+    backward).  Traffic records are stored and looked up under it."""
+    tag = args.workload
+    if getattr(args, "vec", False):
+        tag += "-vec"
+    if getattr(args, "frame", False):
+        tag += "-frame"
+    if args.workload == "l3mace" and getattr(args, "bwd", "msg") == "sender":
+        tag += "-sender"
+    return tag
 
 
 class Timer:
@@ -512,13 +528,17 @@ def cpu_baseline(spec, sample_nodes):
 # ------------------------------------------------------------ traffic from committed counters
 
 
-def committed_traffic(workload, kernel):
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{kernel}.json")
+def committed_traffic(tag, kernel):
+    """HBM bytes per launch from profiles/traffic_<tag>_<kernel>.json, only if
+    that record was taken for this run tag on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}_{kernel}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha") != kernel_sources_sha(workload):
+    if rec.get("tag", rec.get("workload")) != tag:
+        return None
+    if rec.get("source_sha") != kernel_sources_sha(tag):
         return None        # kernels changed since the counters were taken
     return rec.get("bytes_per_launch")
 
@@ -582,7 +602,8 @@ def main():
                    "pct_hbm_peak": round(100 * wl["kernel_bytes"][k] / (timer.mean_ms(k) * 1e-3) / 1e9
                                          / HBM_PEAK_GBS, 1)}
                for k in wl["kernel_bytes"]}
-    traffic = committed_traffic(args.workload, dom)
+    tag = run_tag(args)
+    traffic = committed_traffic(tag, dom)
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_value, 4),
@@ -593,7 +614,7 @@ def main():
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "wall_s": round(wall, 3), "kernel_sources_sha": kernel_sources_sha(args.workload),
+        "wall_s": round(wall, 3), "run_tag": tag, "kernel_sources_sha": kernel_sources_sha(tag),
     }
     if wl.get("kernel_flops"):
         # the second bound: fp32 VALU arithmetic of the same kernel

@@ -56,12 +56,19 @@
  * indices are undefined behaviour; conv_tp_check_graph validates a graph.
  * On a non-zero status, conv_tp_last_error() returns a message (per thread).
  *
+ * Degrees.  l_in, l_sh and l_out are independent, each 0..3 (64 triples;
+ * MACE's first layer, for instance, has scalar inputs: l_in = 0).  Paths with
+ * no admissible l3 <= l_out or l2 <= l_sh do not exist; output blocks that no
+ * path reaches are exact zeros.
+ *
  * Determinism.  algo 0 (CSR forward) and the backward sum in a fixed order
  * and are bitwise reproducible.  On grids of fewer than 4096 waves each
  * node's edge list is split between two workgroups whose two partial sums are
  * added with fp32 atomics onto a zeroed output; two addends onto zero give
- * the same result in either order, so this keeps the guarantee.  algo 1
- * (edge-parallel atomics) is not reproducible.
+ * the same result in either order, so this keeps the guarantee.  The same
+ * holds for the channel sums (dY, dvec, g_y) above 512 channels, which two
+ * channel tiles of at most 512 channels each add into a zeroed output.  algo
+ * 1 (edge-parallel atomics) is not reproducible.
  */
 #ifndef CONVTP_H
 #define CONVTP_H
@@ -75,9 +82,8 @@ extern "C" {
 enum {
     CTP_OK = 0,
     CTP_EINVAL = 1,        /* null pointer, negative size, bad enum value */
-    CTP_EUNSUPPORTED = 2,  /* degree outside 0..3, unequal degrees, channels outside 1..1024,
-                              backward channel count above its limit, algo 1 or 2 in the backward,
-                              algo 2 with Y given or variant 1 */
+    CTP_EUNSUPPORTED = 2,  /* degree outside 0..3, channels above 1024, algo 1 or 2 in a backward,
+                              algo 2 with Y given or variant 1, edge vectors where only Y is taken */
     CTP_EALIGN = 3,        /* a feature/weight array not 16-byte aligned, an index array not 4-byte aligned */
     CTP_EHIP = 4,          /* HIP launch or runtime error (message from hipGetErrorString) */
     CTP_EGRAPH = 5         /* graph arguments inconsistent (e.g. edges without nodes) */
@@ -89,7 +95,7 @@ typedef struct conv_tp_problem {
     int32_t channels;  /* C, 1..1024 */
     int32_t l_in;      /* max degree of x, 0..3 */
     int32_t l_sh;      /* max degree of Y, 0..3 */
-    int32_t l_out;     /* max degree of out, 0..3 (this build: l_in = l_sh = l_out) */
+    int32_t l_out;     /* max degree of out, 0..3 (independent of l_in and l_sh) */
     int32_t y_mode;    /* 0: Y[E][D_sh] given; 1: vec[E][3] given, Y evaluated in-kernel */
     int32_t algo;      /* 0: CSR segmented sum, deterministic; 1: edge-parallel atomics (forward only);
                           2: CSR in each edge's own frame (forward only, y_mode 1, variant 0) */
@@ -136,11 +142,13 @@ int32_t conv_tp_coupling(int32_t l1, int32_t l2, int32_t l3, double *out);
 int32_t conv_tp_fwd(const conv_tp_problem *prob, const float *x, const float *y_or_vec, const float *w,
                     const int32_t *row_ptr, const int32_t *senders, float *out, void *stream);
 
-/* Backward for upstream gradient grad_out = dL/dout: writes dx, dw and dY
+/* Backward for upstream gradient grad_out = dL/dout (the exact VJP of the
+ * forward, FlashCart's section on symbolic VJPs): writes dx, dw and dY
  * (y_mode 0) or dvec = (dY/dvec)^T dY (y_mode 1).  One workgroup per sender
- * walks its out-edges through (send_ptr, send_perm, send_recv), one channel
- * per lane, so every channel of a sender is in one workgroup and dY is summed
- * in a fixed order.  algo must be 0; C <= 512. */
+ * and channel tile walks the sender's out-edges through (send_ptr, send_perm,
+ * send_recv), one channel per lane; dY is summed over the tile's channels in a
+ * fixed order (up to 512 channels in one tile; two tiles above that, see
+ * Determinism).  algo must be 0; C up to 1024. */
 int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y_or_vec,
                     const float *w, const int32_t *row_ptr, const int32_t *senders, const int32_t *send_ptr,
                     const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec,
@@ -153,8 +161,8 @@ int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const fl
  * overwritten; one workgroup per receiver keeps grad_out's row in registers
  * and sums over channels in a fixed order: bitwise equal to conv_tp_bwd's dY.
  * For recomputing dY where dx and dw are not needed (the edge-vector VJP of
- * the VJP).  y_mode must be 0, algo 0, C <= 512 (CTP_EUNSUPPORTED otherwise);
- * both variants. */
+ * the VJP).  y_mode must be 0 and algo 0 (CTP_EUNSUPPORTED otherwise); both
+ * variants, C up to 1024. */
 int32_t conv_tp_bwd_dy(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *w,
                        const int32_t *row_ptr, const int32_t *senders, float *dy, void *stream);
 
@@ -163,8 +171,10 @@ int32_t conv_tp_bwd_dy(const conv_tp_problem *prob, const float *grad_out, const
  * checks, CTP_EINVAL for a null bytes pointer. */
 int32_t conv_tp_bwd_msg_workspace(const conv_tp_problem *prob, int64_t *bytes);
 
-/* The same backward (same arguments, outputs and math as conv_tp_bwd, e3j's
- * backward section) in two passes through a caller-owned device workspace
+/* The same backward (same arguments, outputs and math as conv_tp_bwd: the
+ * exact VJP of FlashCart's section on symbolic VJPs; e3j's abstract reports
+ * its kernels for the backward pass too) in two passes through a caller-owned
+ * device workspace
  * msg[E][D_in][C] (CSR edge order, 16-byte aligned, at least
  * conv_tp_bwd_msg_workspace bytes, else CTP_EINVAL; contents on entry are
  * ignored and overwritten).  Pass 1, one workgroup per receiver i: G[i] is
@@ -176,8 +186,8 @@ int32_t conv_tp_bwd_msg_workspace(const conv_tp_problem *prob, int64_t *bytes);
  * components at l = 3), so reading G once per receiver instead of once per
  * edge moves fewer bytes; for variant 0 conv_tp_bwd moves fewer.  dw and dY
  * are bitwise those of conv_tp_bwd; dx differs only in the order of its fp32
- * additions (per edge, then over edges) and is reproducible.  algo 0; C <= 512.
- * Calls that share a workspace must not overlap. */
+ * additions (per edge, then over edges) and is reproducible.  algo 0; C up to
+ * 1024.  Calls that share a workspace must not overlap. */
 int32_t conv_tp_bwd_msg(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y_or_vec,
                         const float *w, const int32_t *row_ptr, const int32_t *senders, const int32_t *send_ptr,
                         const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw,
@@ -192,9 +202,10 @@ int32_t conv_tp_bwd_msg(const conv_tp_problem *prob, const float *grad_out, cons
  *   g_x = dx with (w, Y) -> (a_w, Y) plus (w, a_y); g_w = dw with x -> a_x plus
  *   Y -> a_y; g_y = dY with x -> a_x plus w -> a_w.
  * Layouts and graph arrays as for conv_tp_bwd (a_x like x, a_w like w, a_y
- * like Y).  y_mode must be 0 and algo 0 (CTP_EUNSUPPORTED otherwise); C <= 512.
- * Every output is written once in a fixed order (bitwise reproducible).  For
- * edge vectors see conv_tp_sh_jvp / conv_tp_sh_bwd_bwd below. */
+ * like Y, g_grad like grad_out); both variants.  y_mode must be 0 and algo 0
+ * (CTP_EUNSUPPORTED otherwise); C up to 1024.  Every output is written once in
+ * a fixed order (bitwise reproducible; above 512 channels g_y as in
+ * Determinism).  For edge vectors see conv_tp_sh_jvp / conv_tp_sh_bwd_bwd. */
 int32_t conv_tp_bwd_bwd(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y,
                         const float *w, const float *a_x, const float *a_w, const float *a_y, const int32_t *row_ptr,
                         const int32_t *senders, const int32_t *send_ptr, const int32_t *send_perm,
@@ -222,10 +233,11 @@ int32_t conv_tp_sh_jvp(int32_t n_edges, int32_t l_sh, const float *vec, const fl
 int32_t conv_tp_sh_bwd_bwd(int32_t n_edges, int32_t l_sh, const float *vec, const float *dY, const float *a_vec,
                            const float *g_y, float *g_vec, void *stream);
 
-/* Sender-sorted transpose of a CSR-by-receiver graph: send_ptr[N+1],
- * send_perm[E] (CSR edge ids, ascending within each sender) and
- * send_recv[E] (receiver of each).  Integer work, bit-exact and
- * deterministic.  The graph must be valid (conv_tp_check_graph); for an
+/* Sender-sorted transpose of a CSR-by-receiver graph (the ordering of edges
+ * by sender that FlashCart's section 4 names for deterministic gradients of
+ * shared inputs): send_ptr[N+1], send_perm[E] (CSR edge ids, ascending within
+ * each sender) and send_recv[E] (receiver of each).  Integer work, bit-exact
+ * and deterministic.  The graph must be valid (conv_tp_check_graph); for an
  * invalid one the result is undefined but nothing outside the three output
  * arrays is written. */
 int32_t conv_tp_build_transpose(int32_t n_nodes, int32_t n_edges, const int32_t *row_ptr, const int32_t *senders,
@@ -283,7 +295,9 @@ int32_t conv_tp_stream_probe(int32_t kind, const float *src, float *dst, int64_t
 const char *conv_tp_last_error(void);
 
 /* ABI version (major * 100 + minor): 101 added conv_tp_problem.variant, 102
- * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward), 104 conv_tp_bwd_dy. */
+ * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward), 104 conv_tp_bwd_dy, 105
+ * independent degrees, up to 1024 channels in every backward and variant 1
+ * in conv_tp_bwd_bwd. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

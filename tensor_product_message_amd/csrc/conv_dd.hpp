@@ -16,29 +16,23 @@
 // per-edge coupling tables T(Y) and T(aY) in LDS; k_dd_send walks each
 // sender's out-edges like the backward.  Both write every output once in a
 // fixed order: results are bitwise reproducible.
+//
+// Variant 1 (per-path output slots) takes the same code: each path reads and
+// writes its own block of G, and the sender kernel walks the backward's path
+// groups.  Above 512 channels the sender kernel runs as two channel tiles that
+// add their partial gY into a zeroed gY (two addends onto zero: order-free).
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace ctp {
-namespace {
+namespace conv {
 
-__constant__ SlotTab<0> kDdSlot0 = make_slot_tab<0>();
-__constant__ SlotTab<1> kDdSlot1 = make_slot_tab<1>();
-__constant__ SlotTab<2> kDdSlot2 = make_slot_tab<2>();
-__constant__ SlotTab<3> kDdSlot3 = make_slot_tab<3>();
-
-template <int L>
-__device__ __forceinline__ const SlotDev* dd_slot_tab() {
-    if constexpr (L == 0) return kDdSlot0.s;
-    else if constexpr (L == 1) return kDdSlot1.s;
-    else if constexpr (L == 2) return kDdSlot2.s;
-    else return kDdSlot3.s;
-}
-
-constexpr int kRecvMaxThreads = 256;
-constexpr int kSendMaxThreads = 512;
+constexpr int kDdRecvMaxThreads = 256;
+constexpr int kDdSendMaxThreads = 512;
 
 template <int D>
 __device__ __forceinline__ void load_row(rsrc_t r, uint32_t voff, uint32_t c4, float (&v)[D]) {
@@ -74,13 +68,12 @@ __device__ __forceinline__ void store_row_stream(rsrc_t r, uint32_t voff, uint32
 // Per edge and path p:  s1 = w_p ax + aw_p x,  s2 = w_p x  (x rows of the sender),
 //   gG[l3 m3] += sum_m1 T_p(Y)[m1][m3] s1[m1] + T_p(aY)[m1][m3] s2[m1].
 
-template <int L>
-__global__ void __launch_bounds__(kRecvMaxThreads)
+template <class S>
+__global__ void __launch_bounds__(kDdRecvMaxThreads)
 k_dd_recv(int C, const float* __restrict__ x, const float* __restrict__ ax, const float* __restrict__ Y,
           const float* __restrict__ aY, const float* __restrict__ w, const float* __restrict__ aw,
           const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ gG) {
-    using S = Spec<L, L, L>;
-    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
+    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::DO, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
     __shared__ __attribute__((aligned(16))) float sT[2][2][NTP];   // [buffer][T(Y), T(aY)]
     __shared__ float sY[2][2][16];
     __shared__ SlotDev sTab[NT];
@@ -97,7 +90,7 @@ k_dd_recv(int C, const float* __restrict__ x, const float* __restrict__ ax, cons
     const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
     if (e0 < e1) {
         {
-            const SlotDev* tab = dd_slot_tab<L>();
+            const SlotDev* tab = slot_tab<S>();
             for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
         }
         float xv[D1], axv[D1], wv[P], awv[P];
@@ -118,8 +111,8 @@ k_dd_recv(int C, const float* __restrict__ x, const float* __restrict__ ax, cons
             }
         }
         __syncthreads();
-        build_T_lds<L>(sT[0][0], sY[0][0], sTab, tid, nth);
-        build_T_lds<L>(sT[0][1], sY[0][1], sTab, tid, nth);
+        build_T_lds<S>(sT[0][0], sY[0][0], sTab, tid, nth);
+        build_T_lds<S>(sT[0][1], sY[0][1], sTab, tid, nth);
         __syncthreads();
         for (int e = e0; e < e1; ++e) {
             const int buf = (e - e0) & 1;
@@ -129,7 +122,7 @@ k_dd_recv(int C, const float* __restrict__ x, const float* __restrict__ ax, cons
             static_for<P>([&](auto pI) __attribute__((always_inline)) {
                 constexpr int p = decltype(pI)::value;
                 constexpr PathL q = S::paths[p];
-                constexpr int n1 = 2 * q.l1 + 1, o1 = q.l1 * q.l1, o3 = q.l3 * q.l3;
+                constexpr int n1 = 2 * q.l1 + 1, o1 = q.l1 * q.l1, o3 = S::out_off[p];
                 constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
                 float s1[n1], s2[n1];
 #pragma unroll
@@ -143,7 +136,7 @@ k_dd_recv(int C, const float* __restrict__ x, const float* __restrict__ ax, cons
                     acc[o3 + s.m3] = __builtin_fmaf(slot_value<t>(T0), s1[s.m1], acc[o3 + s.m3]);
                     acc[o3 + s.m3] = __builtin_fmaf(slot_value<t>(T1), s2[s.m1], acc[o3 + s.m3]);
                 });
-                if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0x100);
+                if constexpr (S::P >= 20) __builtin_amdgcn_sched_barrier(0x100);
             });
             // the sums are pinned so the next edge's loads cannot be hoisted above
             // the arithmetic that still needs the registers they reuse
@@ -160,8 +153,8 @@ k_dd_recv(int C, const float* __restrict__ x, const float* __restrict__ ax, cons
                     sY[buf ^ 1][1][tt] = an;
                 }
                 __syncthreads();
-                build_T_lds<L>(sT[buf ^ 1][0], sY[buf ^ 1][0], sTab, tt, nth);
-                build_T_lds<L>(sT[buf ^ 1][1], sY[buf ^ 1][1], sTab, tt, nth);
+                build_T_lds<S>(sT[buf ^ 1][0], sY[buf ^ 1][0], sTab, tt, nth);
+                build_T_lds<S>(sT[buf ^ 1][1], sY[buf ^ 1][1], sTab, tt, nth);
                 __syncthreads();
             }
         }
@@ -178,24 +171,24 @@ k_dd_recv(int C, const float* __restrict__ x, const float* __restrict__ ax, cons
 //                = sum_c sum_p B_p(w_p ax + aw_p x, g)[m2]   (B is linear in a),
 //   B_p(a, g)[m2] = sum_{m1,m3} C_p[m1][m2][m3] a[m1] g[m3].
 
-template <int L>
-__global__ void __launch_bounds__(kSendMaxThreads)
+template <class S>
+__global__ void __launch_bounds__(kDdSendMaxThreads)
 k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ ax,
           const float* __restrict__ Y, const float* __restrict__ aY, const float* __restrict__ w,
           const float* __restrict__ aw, const int* __restrict__ send_ptr, const int* __restrict__ send_perm,
           const int* __restrict__ send_recv, float* __restrict__ gx, float* __restrict__ gw,
-          float* __restrict__ gY) {
-    using S = Spec<L, L, L>;
-    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::D3, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
+          float* __restrict__ gY, int gy_atomic) {
+    constexpr int D1 = S::D1, D2 = S::D2, D3 = S::DO, P = S::P, NT = S::NT, NTP = (NT + 3) & ~3;
     __shared__ __attribute__((aligned(16))) float sT[2][2][NTP];
     __shared__ float sY[2][2][16];
-    __shared__ float sRed[kSendMaxThreads / 64][16];
+    __shared__ float sRed[kDdSendMaxThreads / 64][16];
     __shared__ SlotDev sTab[NT];
 
     const int j = blockIdx.x;
     const int tid = threadIdx.x, nth = blockDim.x;
     const int nwaves = nth >> 6;
-    const uint32_t voff = opaque_lane(tid < C ? (uint32_t)tid * 4u : kOffLane);
+    const int c0 = blockIdx.y * nth + tid;
+    const uint32_t voff = opaque_lane(c0 < C ? (uint32_t)c0 * 4u : kOffLane);
 
     float xv[D1], axv[D1], gxa[D1];
     {
@@ -209,7 +202,7 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
     const int k0 = send_ptr[j], k1 = send_ptr[j + 1];
     if (k0 < k1) {
         {
-            const SlotDev* tab = dd_slot_tab<L>();
+            const SlotDev* tab = slot_tab<S>();
             for (int t = tid; t < NT; t += nth) sTab[t] = tab[t];
         }
         float gv[D3], wv[P], awv[P];
@@ -229,8 +222,8 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
             }
         }
         __syncthreads();
-        build_T_lds<L>(sT[0][0], sY[0][0], sTab, tid, nth);
-        build_T_lds<L>(sT[0][1], sY[0][1], sTab, tid, nth);
+        build_T_lds<S>(sT[0][0], sY[0][0], sTab, tid, nth);
+        build_T_lds<S>(sT[0][1], sY[0][1], sTab, tid, nth);
         __syncthreads();
 
         for (int k = k0; k < k1; ++k) {
@@ -242,14 +235,13 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
             float gya[16];
 #pragma unroll
             for (int d = 0; d < 16; ++d) gya[d] = 0.0f;
-            static_for<L + 1>([&](auto l1I) __attribute__((always_inline)) {
-                constexpr int l1 = decltype(l1I)::value;
-                static_for<L + 1>([&](auto l3I) __attribute__((always_inline)) {
-                    constexpr int l3 = decltype(l3I)::value;
-                    constexpr PairPaths pp = pair_paths<S>(l1, l3);
-                    if constexpr (pp.n > 0) {
+            static_for<S::NG>([&](auto gI) __attribute__((always_inline)) {
+                constexpr PathGroup pp = S::groups[decltype(gI)::value];
+                constexpr int l1 = pp.l1;
+                {
+                    {
                         constexpr int n1 = 2 * l1 + 1;
-                        constexpr int o1 = l1 * l1, o3 = l3 * l3;
+                        constexpr int o1 = l1 * l1, o3 = pp.o3;   // o3: the group's block of G
                         // (a) v, v', gw and gx for the pair's paths
                         static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
                             constexpr int p = pp.p[decltype(kI)::value];
@@ -280,7 +272,7 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
                                 gxa[o1 + a] = __builtin_fmaf(wv[p], v2[a], gxa[o1 + a]);
                                 pin_f32(gxa[o1 + a]);
                             }
-                            if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+                            if constexpr (S::P >= 20) __builtin_amdgcn_sched_barrier(0);
                         });
                         __builtin_amdgcn_sched_barrier(0);
                         // (b) gY per path: u_p = w_p ax + aw_p x, then B_p(u_p, g) added into gY.
@@ -307,11 +299,11 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
                             });
 #pragma unroll
                             for (int q = 0; q < n2; ++q) gya[o2 + q] += B[q];
-                            if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+                            if constexpr (S::P >= 20) __builtin_amdgcn_sched_barrier(0);
                         });
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                });
+                }
             });
 
             // next edge's rows into the registers just freed (zeros after the last)
@@ -335,13 +327,14 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
             }
             __syncthreads();
             if (has_next) {
-                build_T_lds<L>(sT[buf ^ 1][0], sY[buf ^ 1][0], sTab, tt, nth);
-                build_T_lds<L>(sT[buf ^ 1][1], sY[buf ^ 1][1], sTab, tt, nth);
+                build_T_lds<S>(sT[buf ^ 1][0], sY[buf ^ 1][0], sTab, tt, nth);
+                build_T_lds<S>(sT[buf ^ 1][1], sY[buf ^ 1][1], sTab, tt, nth);
             }
             if (tt < D2) {
                 float tot = sRed[0][tt];
                 for (int q = 1; q < nwaves; ++q) tot += sRed[q][tt];
-                gY[e_cur * D2 + tt] = tot;
+                if (gy_atomic) unsafeAtomicAdd(gY + e_cur * D2 + tt, tot);
+                else gY[e_cur * D2 + tt] = tot;
             }
             __syncthreads();
         }
@@ -349,37 +342,27 @@ k_dd_send(int C, const float* __restrict__ G, const float* __restrict__ x, const
     store_row_stream<D1>(make_row(gx + (long)j * D1 * C, (long)D1 * C), voff, opaque_u32((uint32_t)C * 4u), gxa);
 }
 
-template <int L>
-hipError_t dd_L(const DoubleArgs& a, hipStream_t st) {
+template <class S>
+hipError_t dd_launch(const DoubleArgs& a, hipStream_t st) {
     // receivers: one channel per lane, up to 4 waves per tile
     {
         const int need = (a.C + 63) / 64;
-        const int waves = need < kRecvMaxThreads / 64 ? need : kRecvMaxThreads / 64;
+        const int waves = need < kDdRecvMaxThreads / 64 ? need : kDdRecvMaxThreads / 64;
         const int tiles = (need + waves - 1) / waves;
-        hipLaunchKernelGGL(k_dd_recv<L>, dim3(a.n_nodes, tiles), dim3(64 * waves), 0, st, a.C, a.x, a.ax, a.y,
+        hipLaunchKernelGGL((k_dd_recv<S>), dim3(a.n_nodes, tiles), dim3(64 * waves), 0, st, a.C, a.x, a.ax, a.y,
                            a.ay, a.w, a.aw, a.row_ptr, a.senders, a.g_grad);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
-    // senders: every channel of a sender in one workgroup (fixed-order gY)
-    const int waves = (a.C + 63) / 64;
-    hipLaunchKernelGGL(k_dd_send<L>, dim3(a.n_nodes), dim3(64 * waves), 0, st, a.C, a.grad, a.x, a.ax, a.y, a.ay,
-                       a.w, a.aw, a.send_ptr, a.send_perm, a.send_recv, a.g_x, a.g_w, a.g_y);
+    // senders: the channels of a sender in one workgroup per tile (fixed-order gY)
+    const int tiles = (a.C + kDdSendMaxThreads - 1) / kDdSendMaxThreads;
+    const int waves = ((a.C + tiles - 1) / tiles + 63) / 64;
+    if (tiles > 1 && a.n_edges > 0)
+        hipLaunchKernelGGL(k_fill0, dim3(1024), dim3(256), 0, st, a.g_y, (long)a.n_edges * S::D2);
+    hipLaunchKernelGGL((k_dd_send<S>), dim3(a.n_nodes, tiles), dim3(64 * waves), 0, st, a.C, a.grad, a.x, a.ax, a.y,
+                       a.ay, a.w, a.aw, a.send_ptr, a.send_perm, a.send_recv, a.g_x, a.g_w, a.g_y,
+                       (int)(tiles > 1));
     return hipGetLastError();
 }
 
-}  // namespace
-
-bool dd_supports_channels(int C) { return (C + 63) / 64 <= kSendMaxThreads / 64; }
-
-hipError_t launch_double_bwd(const DoubleArgs& a, hipStream_t st) {
-    if (a.n_nodes == 0) return hipSuccess;
-    switch (a.L) {
-        case 0: return dd_L<0>(a, st);
-        case 1: return dd_L<1>(a, st);
-        case 2: return dd_L<2>(a, st);
-        case 3: return dd_L<3>(a, st);
-    }
-    return hipErrorInvalidValue;
-}
-
+}  // namespace conv
 }  // namespace ctp

@@ -11,19 +11,23 @@
 // coupling non-zeros, exactly as the backward does for dY (same operations in
 // the same order, so the same bits), then sums over channels (lanes by
 // fixed-order halving, waves through LDS in wave order).  No T, no LDS tables.
+// Above 512 channels two channel tiles add their partial sums into a zeroed
+// dY (two addends onto zero: the same bits in either order).
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace ctp {
-namespace {
+namespace conv {
 
-constexpr int kDyMaxThreads = 512;   // all channels of one receiver (C <= 512)
+constexpr int kDyMaxThreads = 512;   // channels of one tile
 
 // dya[l2 m2] += sum_p w_p B_p[m2], B_p[m2] = sum C_p[m1][m2][m3] x[m1] g[m3],
 // grouped as the backward's groups (paths reading one block of G).
-template <int L, class S>
+template <class S>
 __device__ __forceinline__ void edge_dy(const float (&xv)[S::D1], const float (&gv)[S::DO], const float (&wv)[S::P],
                                         float (&dya)[16]) {
     static_for<S::NG>([&](auto gI) __attribute__((always_inline)) {
@@ -49,7 +53,7 @@ __device__ __forceinline__ void edge_dy(const float (&xv)[S::D1], const float (&
                         B[kk][nzv.m2] = __builtin_fmaf(nzv.c, p3[nzv.m3], B[kk][nzv.m2]);
                 });
             });
-            if constexpr (L >= 3) __builtin_amdgcn_sched_barrier(0);
+            if constexpr (S::P >= 20) __builtin_amdgcn_sched_barrier(0);
         });
         static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
             constexpr int kk = decltype(kI)::value;
@@ -67,11 +71,10 @@ __device__ __forceinline__ float dy_ld(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, Aux));
 }
 
-template <int L, int V>
+template <class S>
 __global__ void __launch_bounds__(kDyMaxThreads)
 k_bwd_dy(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ w,
-         const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ dy) {
-    using S = Spec<L, L, L, V>;
+         const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ dy, int dy_atomic) {
     constexpr int D1 = S::D1, D2 = S::D2, DO = S::DO, P = S::P;
     __shared__ float sRed[kDyMaxThreads / 64][16];
 
@@ -79,7 +82,8 @@ k_bwd_dy(int C, const float* __restrict__ G, const float* __restrict__ x, const 
     const int k0 = row_ptr[i], k1 = row_ptr[i + 1];
     if (k0 >= k1) return;   // the whole workgroup: no in-edges
     const int tid = threadIdx.x, nth = blockDim.x, nwaves = nth >> 6, ln = tid & 63;
-    const uint32_t voff = opaque_lane(tid < C ? (uint32_t)tid * 4u : kOffLane);   // no channel: loads 0
+    const int c0 = blockIdx.y * nth + tid;
+    const uint32_t voff = opaque_lane(c0 < C ? (uint32_t)c0 * 4u : kOffLane);   // no channel: loads 0
 
     float gv[DO], xv[D1], wv[P];
     {
@@ -99,7 +103,7 @@ k_bwd_dy(int C, const float* __restrict__ G, const float* __restrict__ x, const 
         float dya[16];
 #pragma unroll
         for (int d = 0; d < 16; ++d) dya[d] = 0.0f;
-        edge_dy<L, S>(xv, gv, wv, dya);
+        edge_dy<S>(xv, gv, wv, dya);
 #pragma unroll
         for (int d = 0; d < D2; ++d) pin_f32(dya[d]);
         // the next edge's rows into the registers just used (zeros after the last)
@@ -121,39 +125,22 @@ k_bwd_dy(int C, const float* __restrict__ G, const float* __restrict__ x, const 
         if (tid < D2) {
             float tot = sRed[0][tid];
             for (int q = 1; q < nwaves; ++q) tot += sRed[q][tid];
-            dy[(long)k * D2 + tid] = tot;
+            if (dy_atomic) unsafeAtomicAdd(dy + (long)k * D2 + tid, tot);
+            else dy[(long)k * D2 + tid] = tot;
         }
         __syncthreads();
     }
 }
 
-template <int L, int V>
+template <class S>
 hipError_t dy_launch(const LaunchArgs& a, hipStream_t st) {
-    const int waves = (a.C + 63) / 64;
-    hipLaunchKernelGGL((k_bwd_dy<L, V>), dim3(a.n_nodes), dim3(64 * waves), 0, st, a.C, a.grad, a.x, a.w,
-                       a.row_ptr, a.senders, a.dy);
+    const int tiles = (a.C + kDyMaxThreads - 1) / kDyMaxThreads;
+    const int waves = ((a.C + tiles - 1) / tiles + 63) / 64;
+    if (tiles > 1) hipLaunchKernelGGL(k_fill0, dim3(1024), dim3(256), 0, st, a.dy, (long)a.n_edges * S::D2);
+    hipLaunchKernelGGL((k_bwd_dy<S>), dim3(a.n_nodes, tiles), dim3(64 * waves), 0, st, a.C, a.grad, a.x, a.w,
+                       a.row_ptr, a.senders, a.dy, (int)(tiles > 1));
     return hipGetLastError();
 }
 
-template <int L>
-hipError_t dy_L(const LaunchArgs& a, hipStream_t st) {
-    if (a.variant == kVariantSlots) return dy_launch<L, kVariantSlots>(a, st);
-    return dy_launch<L, kVariantSummed>(a, st);
-}
-
-}  // namespace
-
-bool dy_supports_channels(int C) { return (C + 63) / 64 <= kDyMaxThreads / 64; }
-
-hipError_t launch_bwd_dy(const LaunchArgs& a, hipStream_t st) {
-    if (a.n_nodes == 0 || a.n_edges == 0) return hipSuccess;
-    switch (a.L) {
-        case 0: return dy_L<0>(a, st);
-        case 1: return dy_L<1>(a, st);
-        case 2: return dy_L<2>(a, st);
-        case 3: return dy_L<3>(a, st);
-    }
-    return hipErrorInvalidValue;
-}
-
+}  // namespace conv
 }  // namespace ctp

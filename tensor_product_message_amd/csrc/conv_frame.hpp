@@ -27,13 +27,17 @@
 // per lane, edges in CSR order with the same rotating prefetch as the direct
 // forward; D of the next edge is built into the other LDS buffer after each
 // edge.  SPLIT (small grids) halves each edge list as in the direct forward.
+// With unequal degrees x is rotated up to l_in, the result back up to l_out,
+// and the rotations are built up to the larger of the two.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace ctp {
-namespace {
+namespace conv {
 
 constexpr int kFrameThreads = 256;
 constexpr int kDirs = 7;                       // fixed directions v_j
@@ -144,8 +148,7 @@ constexpr FrameTab make_frame_tab() {
     return t;
 }
 
-__constant__ FrameTab kFrameTab = make_frame_tab();
-__constant__ ShTab kFrameSh = make_sh_tab();   // this file's copy of the harmonic coefficients
+static __constant__ FrameTab kFrameTab = make_frame_tab();
 
 // Y_{l2,0}(z-hat) = sqrt((2 l2 + 1) / 4pi).
 constexpr float y_pole(int l2) {
@@ -198,7 +201,7 @@ __device__ __forceinline__ bool frame_rotation(float vx, float vy, float vz, flo
     return true;
 }
 
-// Builds D^1..D^3 of edge vector vp into sD (kDPad floats) in two lane-parallel
+// Builds D^1..D^L of edge vector vp into sD (kDPad floats) in two lane-parallel
 // phases through sYR (directions, harmonic coefficients and P_l from their
 // LDS copies: no global loads on the per-edge path); returns (uniformly)
 // whether the vector is non-zero.  Leaves the workgroup synchronised.  (Moving
@@ -246,14 +249,14 @@ constexpr int dflat(int l, int a, int b) {
 
 // One edge in its frame: x' = D x, m' = sum_p w_p * slice_p(x'), acc += D^T m';
 // the rows of the next edge are loaded into x and w as they are freed.
-template <int L, class S = Spec<L, L, L>>
-__device__ __forceinline__ void edge_frame(float (&acc)[S::D1], float (&xv)[S::D1], float (&wv)[S::P],
+template <class S>
+__device__ __forceinline__ void edge_frame(float (&acc)[S::D3], float (&xv)[S::D1], float (&wv)[S::P],
                                            const float* sD, float f, rsrc_t nx, rsrc_t nw, uint32_t nvoff,
                                            int C) {
-    constexpr int D = S::D1;
+    constexpr int D = S::D1, D3 = S::D3;
     float xr[D];
     xr[0] = xv[0];
-    static_for<L>([&](auto lI) __attribute__((always_inline)) {
+    static_for<S::L1>([&](auto lI) __attribute__((always_inline)) {
         constexpr int l = decltype(lI)::value + 1, n = 2 * l + 1, o = l * l;
         static_for<n>([&](auto aI) __attribute__((always_inline)) {
             constexpr int a = decltype(aI)::value;
@@ -271,9 +274,9 @@ __device__ __forceinline__ void edge_frame(float (&acc)[S::D1], float (&xv)[S::D
 #pragma unroll
         for (int d = 0; d < D; ++d) xv[d] = ld1(nx, nvoff, (uint32_t)d * c4);
     }
-    float mr[D];
+    float mr[D3];
 #pragma unroll
-    for (int d = 0; d < D; ++d) mr[d] = 0.0f;
+    for (int d = 0; d < D3; ++d) mr[d] = 0.0f;
     static_for<S::P>([&](auto pI) __attribute__((always_inline)) {
         constexpr int p = decltype(pI)::value;
         constexpr PathL q = S::paths[p];
@@ -297,7 +300,7 @@ __device__ __forceinline__ void edge_frame(float (&acc)[S::D1], float (&xv)[S::D
     // first rotation live in registers through the path loop
     asm volatile("" ::: "memory");
     acc[0] += mr[0];
-    static_for<L>([&](auto lI) __attribute__((always_inline)) {
+    static_for<S::L3>([&](auto lI) __attribute__((always_inline)) {
         constexpr int l = decltype(lI)::value + 1, n = 2 * l + 1, o = l * l;
         static_for<n>([&](auto aI) __attribute__((always_inline)) {
             constexpr int a = decltype(aI)::value;
@@ -308,15 +311,15 @@ __device__ __forceinline__ void edge_frame(float (&acc)[S::D1], float (&xv)[S::D
         });
     });
 #pragma unroll
-    for (int d = 0; d < D; ++d) pin_f32(acc[d]);
+    for (int d = 0; d < D3; ++d) pin_f32(acc[d]);
 }
 
-template <int L, bool SPLIT>
+template <class S, bool SPLIT>
 __global__ void __launch_bounds__(kFrameThreads)
 k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, const float* __restrict__ w,
             const int* __restrict__ row_ptr, const int* __restrict__ senders, float* __restrict__ out) {
-    using S = Spec<L, L, L>;
-    constexpr int D = S::D1, P = S::P;
+    constexpr int D = S::D1, D3 = S::D3, P = S::P;
+    constexpr int LD = S::L1 > S::L3 ? S::L1 : S::L3;   // rotations needed up to this degree
     __shared__ __attribute__((aligned(16))) float sD[2][kDPad];
     __shared__ float sYR[kDirs][16];
     __shared__ float sP[kDirs][kDEntries];
@@ -328,9 +331,9 @@ k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, c
     const int c0 = blockIdx.y * nth + tid;
     const uint32_t voff = opaque_lane(c0 < C ? (uint32_t)c0 * 4u : kOffLane);
 
-    float acc[D];
+    float acc[D3];
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] = 0.0f;
+    for (int d = 0; d < D3; ++d) acc[d] = 0.0f;
 
     int e0 = row_ptr[i], e1 = row_ptr[i + 1];
     if constexpr (SPLIT) {
@@ -353,9 +356,9 @@ k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, c
         // per-edge constants into LDS once: P_l, the directions, the harmonic coefficients
         for (int t = tid; t < kDirs * kDEntries; t += nth) sP[t / kDEntries][t % kDEntries] = (&kFrameTab.p[0][0])[t];
         if (tid < kDirs * 3) sV[tid / 3][tid % 3] = kFrameTab.v[tid / 3][tid % 3];
-        if (tid < 16) sSh[tid] = kFrameSh.k[tid];
+        if (tid < 16) sSh[tid] = sh_tab().k[tid];
         __syncthreads();
-        bool nonzero = build_frame<L>(vec + 3L * e0, sD[0], sYR, sP, sV, sSh, tid, nth);
+        bool nonzero = build_frame<LD>(vec + 3L * e0, sD[0], sYR, sP, sV, sSh, tid, nth);
         for (int e = e0; e < e1; ++e) {
             const int buf = (e - e0) & 1;
             const bool has_next = e + 1 < e1;
@@ -364,65 +367,43 @@ k_fwd_frame(int C, const float* __restrict__ x, const float* __restrict__ vec, c
             const rsrc_t nx = make_row(x + jn * D * C, (long)D * C);
             const rsrc_t nw = make_row(w + en * P * C, (long)P * C);
             const uint32_t nvoff = has_next ? voff : kOffLane;
-            edge_frame<L>(acc, xv, wv, sD[buf], nonzero ? 1.0f : 0.0f, nx, nw, nvoff, C);
-            if (has_next) nonzero = build_frame<L>(vec + 3 * en, sD[buf ^ 1], sYR, sP, sV, sSh, tid, nth);
+            edge_frame<S>(acc, xv, wv, sD[buf], nonzero ? 1.0f : 0.0f, nx, nw, nvoff, C);
+            if (has_next) nonzero = build_frame<LD>(vec + 3 * en, sD[buf ^ 1], sYR, sP, sV, sSh, tid, nth);
         }
     }
     if constexpr (SPLIT) {
         if (e0 < e1 && c0 < C) {
-            float* o = out + (long)i * D * C + c0;
+            float* o = out + (long)i * D3 * C + c0;
 #pragma unroll
-            for (int d = 0; d < D; ++d) unsafeAtomicAdd(o + (long)d * C, acc[d]);
+            for (int d = 0; d < D3; ++d) unsafeAtomicAdd(o + (long)d * C, acc[d]);
         }
     } else {
-        const rsrc_t orow = make_row(out + (long)i * D * C, (long)D * C);
+        const rsrc_t orow = make_row(out + (long)i * D3 * C, (long)D3 * C);
 #pragma unroll
-        for (int d = 0; d < D; ++d)
+        for (int d = 0; d < D3; ++d)
             st1_stream(orow, voff, (uint32_t)(d * C * 4), acc[d]);
     }
 }
 
-// Zero fill before the split's atomics (a kernel, not a memset, so that the
-// call can be captured in a HIP graph; the library's other fill lives in
-// another translation unit).
-__global__ void k_zero_frame(float* __restrict__ p, long n) {
-    long k = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long stride = (long)gridDim.x * blockDim.x;
-    for (; k < n; k += stride) p[k] = 0.0f;
-}
-
 constexpr long kFrameSplitBelowWaves = 4L * 1024;
 
-template <int L>
-hipError_t frame_L(const LaunchArgs& a, hipStream_t st) {
+template <class S>
+hipError_t frame_launch(const LaunchArgs& a, hipStream_t st) {
     const int waves_needed = (a.C + 63) / 64;
     const int waves = waves_needed < kFrameThreads / 64 ? waves_needed : kFrameThreads / 64;
     const int tiles = (waves_needed + waves - 1) / waves;
     const bool split = (long)a.n_nodes * tiles * waves < kFrameSplitBelowWaves;
     const dim3 block(64 * waves);
     if (split) {
-        const long n = (long)a.n_nodes * (L + 1) * (L + 1) * a.C;
-        hipLaunchKernelGGL(k_zero_frame, dim3(1024), dim3(256), 0, st, a.out, n);
-        hipLaunchKernelGGL((k_fwd_frame<L, true>), dim3(a.n_nodes, tiles, 2), block, 0, st, a.C, a.x, a.y, a.w,
+        hipLaunchKernelGGL(k_fill0, dim3(1024), dim3(256), 0, st, a.out, (long)a.n_nodes * S::D3 * a.C);
+        hipLaunchKernelGGL((k_fwd_frame<S, true>), dim3(a.n_nodes, tiles, 2), block, 0, st, a.C, a.x, a.y, a.w,
                            a.row_ptr, a.senders, a.out);
     } else {
-        hipLaunchKernelGGL((k_fwd_frame<L, false>), dim3(a.n_nodes, tiles), block, 0, st, a.C, a.x, a.y, a.w,
+        hipLaunchKernelGGL((k_fwd_frame<S, false>), dim3(a.n_nodes, tiles), block, 0, st, a.C, a.x, a.y, a.w,
                            a.row_ptr, a.senders, a.out);
     }
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_fwd_frame(const LaunchArgs& a, hipStream_t st) {
-    if (a.n_nodes == 0) return hipSuccess;
-    switch (a.L) {
-        case 0: return frame_L<0>(a, st);
-        case 1: return frame_L<1>(a, st);
-        case 2: return frame_L<2>(a, st);
-        case 3: return frame_L<3>(a, st);
-    }
-    return hipErrorInvalidValue;
-}
-
+}  // namespace conv
 }  // namespace ctp

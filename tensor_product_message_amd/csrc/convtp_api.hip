@@ -65,12 +65,11 @@ int check_problem(const conv_tp_problem* pr, Shape* s) {
     if (pr == nullptr) return fail(CTP_EINVAL, "problem is null");
     if (pr->n_nodes < 0 || pr->n_edges < 0) return fail(CTP_EINVAL, "negative node or edge count");
     if (pr->channels < 1) return fail(CTP_EINVAL, "channels = %d must be >= 1", pr->channels);
-    if (pr->channels > 1024) return fail(CTP_EUNSUPPORTED, "channels = %d above 1024", pr->channels);
+    if (pr->channels > ctp::kMaxChannels)
+        return fail(CTP_EUNSUPPORTED, "channels = %d above %d", pr->channels, ctp::kMaxChannels);
     if (int r = check_degree(pr->l_in, "l_in")) return r;
     if (int r = check_degree(pr->l_sh, "l_sh")) return r;
     if (int r = check_degree(pr->l_out, "l_out")) return r;
-    if (pr->l_in != pr->l_sh || pr->l_sh != pr->l_out)
-        return fail(CTP_EUNSUPPORTED, "degrees (%d,%d,%d) must be equal in this build", pr->l_in, pr->l_sh, pr->l_out);
     if (pr->y_mode != 0 && pr->y_mode != 1) return fail(CTP_EINVAL, "y_mode = %d not 0 or 1", pr->y_mode);
     if (pr->algo < 0 || pr->algo > 2) return fail(CTP_EINVAL, "algo = %d not 0, 1 or 2", pr->algo);
     if (pr->variant != ctp::kVariantSummed && pr->variant != ctp::kVariantSlots)
@@ -89,7 +88,9 @@ int check_problem(const conv_tp_problem* pr, Shape* s) {
 
 ctp::LaunchArgs base_args(const conv_tp_problem* pr) {
     ctp::LaunchArgs a{};
-    a.L = pr->l_in;
+    a.l_in = pr->l_in;
+    a.l_sh = pr->l_sh;
+    a.l_out = pr->l_out;
     a.n_nodes = pr->n_nodes;
     a.n_edges = pr->n_edges;
     a.C = pr->channels;
@@ -107,8 +108,6 @@ int bwd_args(const conv_tp_problem* prob, const float* grad_out, const float* x,
     Shape& s = *sp;
     if (int r = check_problem(prob, &s)) return r;
     if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the backward has only the deterministic algorithm (algo 0)");
-    if (!ctp::bwd_supports_channels(prob->channels))
-        return fail(CTP_EUNSUPPORTED, "backward needs C <= 512, got %d", prob->channels);
     if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
     if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
     if (int r = need(y_or_vec, s.E * s.S, 4, "y_or_vec")) return r;
@@ -178,7 +177,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 104; }
+int32_t conv_tp_version(void) { return 105; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
@@ -262,8 +261,6 @@ int32_t conv_tp_bwd_dy(const conv_tp_problem* prob, const float* grad_out, const
     if (int r = check_problem(prob, &s)) return r;
     if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_dy has only the deterministic algorithm (algo 0)");
     if (prob->y_mode != 0) return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_dy writes dY: y_mode must be 0");
-    if (!ctp::dy_supports_channels(prob->channels))
-        return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_dy needs C <= 512, got %d", prob->channels);
     if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
     if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
     if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;
@@ -313,10 +310,6 @@ int32_t conv_tp_bwd_bwd(const conv_tp_problem* prob, const float* grad_out, cons
     if (int r = check_problem(prob, &s)) return r;
     if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the double backward has only the deterministic algorithm");
     if (prob->y_mode != 0) return fail(CTP_EUNSUPPORTED, "the double backward takes Y (y_mode 0)");
-    if (prob->variant != ctp::kVariantSummed)
-        return fail(CTP_EUNSUPPORTED, "the double backward is built for variant 0 (summed outputs)");
-    if (!ctp::dd_supports_channels(prob->channels))
-        return fail(CTP_EUNSUPPORTED, "double backward needs C <= 512, got %d", prob->channels);
     if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
     if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
     if (int r = need(y, s.E * s.D2, 4, "y")) return r;
@@ -334,7 +327,10 @@ int32_t conv_tp_bwd_bwd(const conv_tp_problem* prob, const float* grad_out, cons
     if (int r = need(g_y, s.E * s.D2, 4, "g_y")) return r;
     if (int r = need(g_grad, s.N * s.D3 * s.C, 16, "g_grad")) return r;
     ctp::DoubleArgs a{};
-    a.L = prob->l_in;
+    a.l_in = prob->l_in;
+    a.l_sh = prob->l_sh;
+    a.l_out = prob->l_out;
+    a.variant = prob->variant;
     a.n_nodes = prob->n_nodes;
     a.n_edges = prob->n_edges;
     a.C = prob->channels;

@@ -24,6 +24,16 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// ------------------------------------------------------------ zero fill
+
+// Zero fill of n floats (a kernel, not a memset, so that calls can be captured
+// in a HIP graph); one copy per translation unit that launches it.
+[[maybe_unused]] static __global__ void k_fill0(float* __restrict__ p, long n) {
+    long k = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (; k < n; k += stride) p[k] = 0.0f;
+}
+
 // ------------------------------------------------------------ per-slot flags
 
 // True if slot t is the first slot of its path that touches m3 (resp. m1):
@@ -84,21 +94,22 @@ struct SlotDev {
     float c1, c2;
 };
 
-template <int L, int V = kVariantSummed>
+// One table per problem spec S (a Spec<L1, L2, L3, V>).
+template <class S>
 struct SlotTab {
-    SlotDev s[Spec<L, L, L, V>::NT];
+    SlotDev s[S::NT];
 };
 
-template <int L, int V = kVariantSummed>
-constexpr SlotTab<L, V> make_slot_tab() {
-    using S = Spec<L, L, L, V>;
-    SlotTab<L, V> r{};
+template <class S>
+constexpr SlotTab<S> make_slot_tab() {
+    SlotTab<S> r{};
     for (int t = 0; t < S::NT; ++t)
         r.s[t] = SlotDev{S::slots[t].y1 | (S::slots[t].y2 << 8), S::slots[t].c1, S::slots[t].c2};
     return r;
 }
 
-template <int L, int V = kVariantSummed>
+// Device copy of S's slot table (defined next to the kernels that use it).
+template <class S>
 __device__ __forceinline__ const SlotDev* slot_tab();
 
 // ------------------------------------------------------------ real spherical harmonics
@@ -416,10 +427,9 @@ __device__ __forceinline__ float sh_load(const float* __restrict__ yv, long e, i
     }
 }
 
-template <int L, int V = kVariantSummed>
+template <class S>
 __device__ __forceinline__ void build_T_lds(float* sT, const float* sY, const SlotDev* tab, int tid, int nth) {
-    constexpr int NT = Spec<L, L, L, V>::NT;
-    for (int t = tid; t < NT; t += nth) {
+    for (int t = tid; t < S::NT; t += nth) {
         const SlotDev s = tab[t];
         sT[t] = s.c1 * sY[s.yy & 0xff] + s.c2 * sY[s.yy >> 8];
     }

@@ -175,8 +175,9 @@ struct PathGroup {
     int p[kMaxL + 1];
 };
 
-template <int L1, int L2, int L3, int V = kVariantSummed>
+template <int L1_, int L2_, int L3_, int V_ = kVariantSummed>
 struct Spec {
+    static constexpr int L1 = L1_, L2 = L2_, L3 = L3_, V = V_;
     static constexpr int D1 = dim_of(L1), D2 = dim_of(L2), D3 = dim_of(L3);
     static constexpr int P = num_paths(L1, L2, L3, V);
     static constexpr int DO = out_dim(L1, L2, L3, V);   // output (and G) components

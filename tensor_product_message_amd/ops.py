@@ -5,11 +5,15 @@ tensor metadata, passes raw device pointers and the current HIP stream, and
 turns a non-zero status into `ConvTPError`.  PyTorch provides device memory
 and streams, nothing else.
 
-Shapes (channel index fastest, D_l = (l+1)^2, P = num_paths(l)):
-    x, out, grad_out, dx : [N, D, C] float32
-    w, dw                : [E, P, C] float32
-    Y, dY                : [E, D]    float32  (y_mode 0)
-    vec, dvec            : [E, 3]    float32  (y_mode 1)
+Degrees: every call takes `lmax`, either one int L (l_in = l_sh = l_out = L)
+or a tuple (l_in, l_sh, l_out), each in 0..3.
+
+Shapes (channel index fastest, D_l = (l+1)^2, P and D_out from `layout`):
+    x, dx                : [N, D_in, C]  float32
+    out, grad_out        : [N, D_out, C] float32 (D_out = D_{l_out} for variant 0)
+    w, dw                : [E, P, C]     float32
+    Y, dY                : [E, D_sh]     float32  (y_mode 0)
+    vec, dvec            : [E, 3]        float32  (y_mode 1)
     row_ptr [N+1], senders [E], send_ptr [N+1], send_perm [E], send_recv [E]: int32
 """
 from __future__ import annotations
@@ -54,6 +58,15 @@ def dim(l: int) -> int:
     return (l + 1) ** 2
 
 
+def degrees(lmax):
+    """(l_in, l_sh, l_out) from an int L or a 3-tuple."""
+    if isinstance(lmax, (tuple, list)):
+        if len(lmax) != 3:
+            raise ValueError("lmax must be an int or (l_in, l_sh, l_out)")
+        return tuple(int(v) for v in lmax)
+    return (int(lmax),) * 3
+
+
 def num_paths(l_in: int, l_sh: int = None, l_out: int = None) -> int:
     l_sh = l_in if l_sh is None else l_sh
     l_out = l_in if l_out is None else l_out
@@ -72,13 +85,14 @@ def paths(l_in: int, l_sh: int = None, l_out: int = None):
     return [tuple(int(v) for v in r) for r in buf]
 
 
-def layout(lmax: int, variant: int = SUMMED):
+def layout(lmax, variant: int = SUMMED):
     """(paths, out_dim) of a variant: the path list in w's order and the
     number of output components per channel."""
+    a, b, c = degrees(lmax)
     n, d = ctypes.c_int32(0), ctypes.c_int32(0)
-    check(lib().conv_tp_layout(variant, lmax, lmax, lmax, ctypes.byref(n), ctypes.byref(d), None))
+    check(lib().conv_tp_layout(variant, a, b, c, ctypes.byref(n), ctypes.byref(d), None))
     buf = np.zeros((n.value, 3), dtype=np.int32)
-    check(lib().conv_tp_layout(variant, lmax, lmax, lmax, ctypes.byref(n), ctypes.byref(d),
+    check(lib().conv_tp_layout(variant, a, b, c, ctypes.byref(n), ctypes.byref(d),
                                buf.ctypes.data_as(ctypes.c_void_p)))
     return [tuple(int(v) for v in r) for r in buf], int(d.value)
 
@@ -139,23 +153,24 @@ def check_graph(n_nodes: int, row_ptr: torch.Tensor, senders: torch.Tensor) -> i
 
 
 def _problem(n_nodes, n_edges, channels, lmax, y_mode, algo, variant=SUMMED) -> Problem:
-    return Problem(n_nodes, n_edges, channels, lmax, lmax, lmax, y_mode, algo, variant)
+    a, b, c = degrees(lmax)
+    return Problem(n_nodes, n_edges, channels, a, b, c, y_mode, algo, variant)
 
 
 def _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant=SUMMED):
     n, e = graph.n_nodes, graph.n_edges
+    l_in, l_sh, _ = degrees(lmax)
     if x.dim() != 3:
         raise ValueError("x must be [N, D, C]")
     c = x.shape[2]
-    _want(x, "x", (n, dim(lmax), c), device=graph.device)
-    _want(y_or_vec, "y_or_vec", (e, dim(lmax) if y_mode == Y_GIVEN else 3), device=graph.device)
-    p = num_paths(lmax) if variant == SUMMED else len(layout(lmax, variant)[0])
-    _want(w, "w", (e, p, c), device=graph.device)
+    _want(x, "x", (n, dim(l_in), c), device=graph.device)
+    _want(y_or_vec, "y_or_vec", (e, dim(l_sh) if y_mode == Y_GIVEN else 3), device=graph.device)
+    _want(w, "w", (e, len(layout(lmax, variant)[0]), c), device=graph.device)
     return n, e, c
 
 
-def out_dim(lmax: int, variant: int = SUMMED) -> int:
-    return dim(lmax) if variant == SUMMED else layout(lmax, variant)[1]
+def out_dim(lmax, variant: int = SUMMED) -> int:
+    return layout(lmax, variant)[1]
 
 
 def conv_tp_fwd(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN, algo: int = ALGO_CSR,
@@ -194,22 +209,23 @@ def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int =
 def conv_tp_bwd_dy(grad_out, x, w, graph: Graph, lmax: int, dy=None, variant: int = SUMMED):
     """dY alone (Y given): the harmonic gradient of conv_tp_bwd without dx and dw."""
     n, e, c = x.shape[0], w.shape[0], x.shape[2]
+    l_in, l_sh, _ = degrees(lmax)
     if graph.n_nodes != n or graph.senders.numel() != e:
         raise ValueError("graph does not match x / w")
-    _want(x, "x", (n, dim(lmax), c))
+    _want(x, "x", (n, dim(l_in), c))
     _want(w, "w", (e, len(layout(lmax, variant)[0]), c), device=x.device)
     _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
-    dy = torch.empty((e, dim(lmax)), dtype=torch.float32, device=x.device) if dy is None else dy
-    _want(dy, "dy", (e, dim(lmax)), device=x.device)
+    dy = torch.empty((e, dim(l_sh)), dtype=torch.float32, device=x.device) if dy is None else dy
+    _want(dy, "dy", (e, dim(l_sh)), device=x.device)
     prob = _problem(n, e, c, lmax, Y_GIVEN, ALGO_CSR, variant)
     check(lib().conv_tp_bwd_dy(ctypes.byref(prob), _p(grad_out), _p(x), _p(w), _p(graph.row_ptr),
                                _p(graph.senders), _p(dy), _stream(x)))
     return dy
 
 
-def conv_tp_bwd_msg_workspace(n_nodes: int, n_edges: int, channels: int, lmax: int, y_mode: int = Y_GIVEN,
+def conv_tp_bwd_msg_workspace(n_nodes: int, n_edges: int, channels: int, lmax, y_mode: int = Y_GIVEN,
                               variant: int = SUMMED) -> int:
-    """Bytes of device workspace conv_tp_bwd_msg needs (E * (lmax+1)^2 * C * 4)."""
+    """Bytes of device workspace conv_tp_bwd_msg needs (E * (l_in+1)^2 * C * 4)."""
     prob = _problem(n_nodes, n_edges, channels, lmax, y_mode, ALGO_CSR, variant)
     out = ctypes.c_int64(0)
     check(lib().conv_tp_bwd_msg_workspace(ctypes.byref(prob), ctypes.byref(out)))
@@ -232,7 +248,7 @@ def conv_tp_bwd_msg(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: i
     _want(dy, "dy", y_or_vec.shape, device=x.device)
     prob = _problem(n, e, c, lmax, y_mode, ALGO_CSR, variant)
     if workspace is None:
-        workspace = torch.empty(max(1, e * dim(lmax) * c), dtype=torch.float32, device=x.device)
+        workspace = torch.empty(max(1, e * dim(degrees(lmax)[0]) * c), dtype=torch.float32, device=x.device)
     if workspace.dtype != torch.float32 or workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous float32 tensor on x's device")
     check(lib().conv_tp_bwd_msg(ctypes.byref(prob), _p(grad_out), _p(x), _p(y_or_vec), _p(w),
@@ -242,11 +258,11 @@ def conv_tp_bwd_msg(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: i
     return dx, dw, dy
 
 
-def conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph: Graph, lmax: int, out=None):
+def conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph: Graph, lmax, out=None, variant: int = SUMMED):
     """VJP of conv_tp_bwd (Y given): gradients (g_x, g_w, g_y, g_grad) of
     <a_x, dx> + <a_w, dw> + <a_y, dY> (see include/convtp.h)."""
-    n, e, c = _shapes(x, Y, w, graph, lmax, Y_GIVEN)
-    _want(grad_out, "grad_out", (n, dim(lmax), c), device=x.device)
+    n, e, c = _shapes(x, Y, w, graph, lmax, Y_GIVEN, variant)
+    _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
     _want(a_x, "a_x", x.shape, device=x.device)
     _want(a_w, "a_w", w.shape, device=x.device)
     _want(a_y, "a_y", Y.shape, device=x.device)
@@ -256,7 +272,7 @@ def conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph: Graph, lmax: int, o
     g_x, g_w, g_y, g_grad = out
     for name, t, ref in (("g_x", g_x, x), ("g_w", g_w, w), ("g_y", g_y, Y), ("g_grad", g_grad, grad_out)):
         _want(t, name, ref.shape, device=x.device)
-    prob = _problem(n, e, c, lmax, Y_GIVEN, ALGO_CSR)
+    prob = _problem(n, e, c, lmax, Y_GIVEN, ALGO_CSR, variant)
     check(lib().conv_tp_bwd_bwd(ctypes.byref(prob), _p(grad_out), _p(x), _p(Y), _p(w), _p(a_x), _p(a_w),
                                 _p(a_y), _p(graph.row_ptr), _p(graph.senders), _p(send_ptr), _p(send_perm),
                                 _p(send_recv), _p(g_x), _p(g_w), _p(g_y), _p(g_grad), _stream(x)))
@@ -353,23 +369,25 @@ def spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, lmax: int, out=None):
     return out
 
 
-def conv_tp_bwd_bwd_vec(grad_out, x, vec, w, a_x, a_w, a_vec, graph: Graph, lmax: int):
+def conv_tp_bwd_bwd_vec(grad_out, x, vec, w, a_x, a_w, a_vec, graph: Graph, lmax, variant: int = SUMMED):
     """VJP of the edge-vector backward: (g_x, g_w, g_vec, g_grad) for
     cotangents (a_x, a_w, a_vec) of (dx, dw, dvec), by the library calls
     include/convtp.h lists (harmonics, the first backward's dY alone, harmonic
     JVP, the double backward, and the harmonic second-order term)."""
-    Y = spherical_harmonics(vec, lmax)
-    dY = conv_tp_bwd_dy(grad_out, x, w, graph, lmax)
-    a_y = spherical_harmonics_jvp(vec, a_vec, lmax)
-    g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph, lmax)
-    g_vec = spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, lmax)
+    l_sh = degrees(lmax)[1]
+    Y = spherical_harmonics(vec, l_sh)
+    dY = conv_tp_bwd_dy(grad_out, x, w, graph, lmax, variant=variant)
+    a_y = spherical_harmonics_jvp(vec, a_vec, l_sh)
+    g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph, lmax, variant=variant)
+    g_vec = spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, l_sh)
     return g_x, g_w, g_vec, g_grad
 
 
 class ConvTPFunction(torch.autograd.Function):
-    """Autograd wrapper: forward = conv_tp_fwd (algo 0); backward = conv_tp_bwd
-    (variant 0) or conv_tp_bwd_msg with a workspace from torch's allocator
-    (variant 1, whose grad_out rows are much wider than x's)."""
+    """Autograd wrapper: forward = conv_tp_fwd (algo 0); backward =
+    ConvTPBackward, itself differentiable once more, so that a loss on forces
+    (gradients of an energy in the edge vectors) trains w and x through
+    torch.autograd.grad(..., create_graph=True)."""
 
     @staticmethod
     def forward(ctx, x, y_or_vec, w, graph, lmax, y_mode, variant):
@@ -380,12 +398,41 @@ class ConvTPFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         x, y_or_vec, w = ctx.saved_tensors
-        bwd = conv_tp_bwd_msg if ctx.variant == SLOTS else conv_tp_bwd
-        dx, dw, dy = bwd(grad_out.contiguous(), x, y_or_vec, w, ctx.graph, ctx.lmax, ctx.y_mode,
-                         variant=ctx.variant)
+        dx, dy, dw = ConvTPBackward.apply(grad_out.contiguous(), x, y_or_vec, w, ctx.graph, ctx.lmax,
+                                          ctx.y_mode, ctx.variant)
         return dx, dy, dw, None, None, None, None
 
 
-def conv_tp(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN, variant: int = SUMMED):
-    """Differentiable fused convolution tensor product."""
+class ConvTPBackward(torch.autograd.Function):
+    """The VJP as a function of (grad_out, x, Y or vec, w), returning
+    (dx, dY or dvec, dw): conv_tp_bwd (variant 0) or conv_tp_bwd_msg with a
+    workspace from torch's allocator (variant 1, whose grad_out rows are much
+    wider than x's).  Its own VJP (the VJP of the VJP) is conv_tp_bwd_bwd, with
+    the harmonics' second-order terms for edge vectors (conv_tp_bwd_bwd_vec)."""
+
+    @staticmethod
+    def forward(ctx, grad_out, x, y_or_vec, w, graph, lmax, y_mode, variant):
+        ctx.save_for_backward(grad_out, x, y_or_vec, w)
+        ctx.graph, ctx.lmax, ctx.y_mode, ctx.variant = graph, lmax, y_mode, variant
+        bwd = conv_tp_bwd_msg if variant == SLOTS else conv_tp_bwd
+        dx, dw, dy = bwd(grad_out, x, y_or_vec, w, graph, lmax, y_mode, variant=variant)
+        return dx, dy, dw
+
+    @staticmethod
+    @torch.autograd.function.once_differentiable
+    def backward(ctx, a_x, a_y, a_w):
+        G, x, y_or_vec, w = ctx.saved_tensors
+        a_x, a_y, a_w = a_x.contiguous(), a_y.contiguous(), a_w.contiguous()
+        if ctx.y_mode == Y_GIVEN:
+            g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd(G, x, y_or_vec, w, a_x, a_w, a_y, ctx.graph, ctx.lmax,
+                                                    variant=ctx.variant)
+        else:
+            g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd_vec(G, x, y_or_vec, w, a_x, a_w, a_y, ctx.graph, ctx.lmax,
+                                                        variant=ctx.variant)
+        return g_grad, g_x, g_y, g_w, None, None, None, None
+
+
+def conv_tp(x, y_or_vec, w, graph: Graph, lmax, y_mode: int = Y_GIVEN, variant: int = SUMMED):
+    """Differentiable fused convolution tensor product (twice differentiable in
+    x, w and Y or vec)."""
     return ConvTPFunction.apply(x, y_or_vec, w, graph, lmax, y_mode, variant)

@@ -42,17 +42,47 @@ def test_fma_counts(ctp):
 
 
 def test_traffic_records_follow_the_sources(tmp_path, monkeypatch):
-    for wl, kern in (("l3fb", "bwd"), ("l3fb", "fwd"), ("l3mace", "bwd"), ("l3dd", "dd"), ("node3", "bwd")):
-        path = os.path.join(ROOT, "profiles", f"traffic_{wl}_{kern}.json")
-        rec = json.load(open(path))
-        got = bench.committed_traffic(wl, kern)
-        if rec["source_sha"] == bench.kernel_sources_sha(wl):
+    for path in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        if not (path.startswith("traffic_") and path.endswith(".json")):
+            continue
+        rec = json.load(open(os.path.join(ROOT, "profiles", path)))
+        tag, kern = rec.get("tag", rec["workload"]), rec["kernel"]
+        assert path == f"traffic_{tag}_{kern}.json"
+        got = bench.committed_traffic(tag, kern)
+        if rec["source_sha"] == bench.kernel_sources_sha(tag):
             assert got == rec["bytes_per_launch"] > 0
         else:
             assert got is None
     # a record taken on other sources is not used
     monkeypatch.setattr(bench, "kernel_sources_sha", lambda workload="l3fb": "0" * 16)
     assert bench.committed_traffic("l3fb", "bwd") is None
+
+
+def test_run_tags_keep_modes_apart(tmp_path, monkeypatch):
+    import argparse
+    A = lambda **kw: argparse.Namespace(**{**dict(workload="l3fb", vec=False, frame=False, bwd="msg"), **kw})  # noqa: E731
+    assert bench.run_tag(A()) == "l3fb"
+    assert bench.run_tag(A(vec=True)) == "l3fb-vec"
+    assert bench.run_tag(A(vec=True, frame=True)) == "l3fb-vec-frame"
+    assert bench.run_tag(A(workload="l3mace", bwd="sender")) == "l3mace-sender"
+    # a record of the Y-given run is never reported for the edge-vector run
+    rec = dict(workload="l3fb", tag="l3fb", kernel="bwd", source_sha=bench.kernel_sources_sha("l3fb"),
+               bytes_per_launch=123)
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic_l3fb_bwd.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_sources_sha", lambda tag="l3fb": rec["source_sha"])
+    assert bench.committed_traffic("l3fb", "bwd") == 123
+    assert bench.committed_traffic("l3fb-vec", "bwd") is None
+    assert bench.committed_traffic("l3fb-vec-frame", "bwd") is None
+
+
+def test_every_kernel_source_is_hashed():
+    csrc = os.path.join(ROOT, "tensor_product_message_amd", "csrc")
+    hashed = set(bench.CONV_SOURCES + bench.COMMON_SOURCES)
+    for f in os.listdir(csrc):
+        if f.startswith(("conv", "device_common", "tables", "kernels")):
+            assert f in hashed, f
 
 
 def test_more_than_one_gpu_is_refused():

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 104
+    assert L.conv_tp_version() == 105
 
 
 def test_paths_match_oracle(capi):
@@ -92,7 +92,7 @@ def _bwd(capi, prob, g=A, x=A, y=A, w=A, rp=A, s=A, sp=A, pe=A, sr=A, dx=A2, dw=
 @pytest.mark.parametrize("kw,code", [
     (dict(n_nodes=-1), 1), (dict(n_edges=-3), 1), (dict(channels=0), 1),
     (dict(channels=1025), 2), (dict(l_in=4, l_sh=4, l_out=4), 2), (dict(l_in=-1), 2),
-    (dict(l_in=1, l_sh=2, l_out=2), 2), (dict(y_mode=2), 1), (dict(algo=7), 1),
+    (dict(l_sh=4), 2), (dict(l_out=4), 2), (dict(l_in=4), 2), (dict(y_mode=2), 1), (dict(algo=7), 1),
     (dict(n_nodes=0, n_edges=5), 5),
 ])
 def test_fwd_rejects_bad_problem(capi, kw, code):
@@ -126,10 +126,33 @@ def test_frame_forward_rejections(capi):
     assert _bwd(capi, _prob(capi, algo=2, y_mode=1)) == capi.CTP_EUNSUPPORTED
 
 
+def _empty(capi, **kw):
+    # N = E = 0: validation runs in full, then nothing is launched (safe without a GPU)
+    return _prob(capi, n_nodes=0, n_edges=0, **kw)
+
+
+@pytest.mark.parametrize("deg", [(0, 3, 3), (1, 3, 2), (3, 2, 1), (2, 2, 2), (0, 0, 3), (3, 0, 0)])
+@pytest.mark.parametrize("channels", [1, 513, 1024])
+def test_every_degree_triple_and_channel_count_is_accepted(capi, deg, channels):
+    a, b, c = deg
+    for variant in (0, 1):
+        for y_mode in (0, 1):
+            p = _empty(capi, channels=channels, l_in=a, l_sh=b, l_out=c, y_mode=y_mode, variant=variant)
+            assert _fwd(capi, p, x=NUL, y=NUL, w=NUL, s=NUL, out=NUL) == capi.CTP_OK
+            assert _bwd(capi, p, g=NUL, x=NUL, y=NUL, w=NUL, s=NUL, pe=NUL, sr=NUL, dx=NUL, dw=NUL,
+                        dy=NUL) == capi.CTP_OK, capi.lib().conv_tp_last_error()
+            assert _bwd_msg(capi, p, ws=NUL, nbytes=0, g=NUL, x=NUL, y=NUL, w=NUL, s=NUL, pe=NUL, sr=NUL,
+                            dx=NUL, dw=NUL, dy=NUL) == capi.CTP_OK
+        p = _empty(capi, channels=channels, l_in=a, l_sh=b, l_out=c, variant=variant)
+        dd = [NUL] * 16
+        dd[7] = dd[9] = A
+        assert _bwd_bwd(capi, p, dd) == capi.CTP_OK
+        assert capi.lib().conv_tp_bwd_dy(ctypes.byref(p), NUL, NUL, NUL, A, NUL, NUL, NUL) == capi.CTP_OK
+
+
 def test_bwd_rejections(capi):
     assert _bwd(capi, _prob(capi, algo=1)) == capi.CTP_EUNSUPPORTED
-    assert _bwd(capi, _prob(capi, channels=1024)) == capi.CTP_EUNSUPPORTED
-    assert _bwd(capi, _prob(capi, channels=513)) == capi.CTP_EUNSUPPORTED
+    assert _bwd(capi, _prob(capi, channels=1025)) == capi.CTP_EUNSUPPORTED
     p = _prob(capi)
     for k in ("g", "x", "y", "w", "rp", "s", "sp", "pe", "sr", "dx", "dw", "dy"):
         assert _bwd(capi, p, **{k: NUL}) == capi.CTP_EINVAL, k
@@ -153,7 +176,7 @@ def test_bwd_msg_rejections(capi):
     assert L.conv_tp_bwd_msg_workspace(ctypes.byref(_prob(capi, variant=3)), ctypes.byref(nb)) == capi.CTP_EINVAL
     assert len(L.conv_tp_bwd_msg.argtypes) == 16   # problem, 12 arrays, workspace, its size, stream
     assert _bwd_msg(capi, _prob(capi, algo=1)) == capi.CTP_EUNSUPPORTED
-    assert _bwd_msg(capi, _prob(capi, channels=513)) == capi.CTP_EUNSUPPORTED
+    assert _bwd_msg(capi, _prob(capi, channels=1025)) == capi.CTP_EUNSUPPORTED
     for k in ("g", "x", "y", "w", "rp", "s", "sp", "pe", "sr", "dx", "dw", "dy"):
         assert _bwd_msg(capi, p, **{k: NUL}) == capi.CTP_EINVAL, k
     assert _bwd_msg(capi, p, nbytes=nb.value - 4) == capi.CTP_EINVAL
@@ -169,7 +192,7 @@ def test_bwd_dy_rejections(capi):
     assert len(L.conv_tp_bwd_dy.argtypes) == 8
     assert f(_prob(capi, y_mode=1), args) == capi.CTP_EUNSUPPORTED
     assert f(_prob(capi, algo=1), args) == capi.CTP_EUNSUPPORTED
-    assert f(_prob(capi, channels=513), args) == capi.CTP_EUNSUPPORTED
+    assert f(_prob(capi, channels=1025), args) == capi.CTP_EUNSUPPORTED
     for k in range(6):
         a = list(args)
         a[k] = NUL
@@ -212,7 +235,7 @@ def test_bwd_bwd_rejections(capi):
     args = [A] * 12 + [A2] * 4      # 12 inputs (grad_out .. send_recv), 4 outputs
     assert _bwd_bwd(capi, _prob(capi, y_mode=1), args) == capi.CTP_EUNSUPPORTED
     assert _bwd_bwd(capi, _prob(capi, algo=1), args) == capi.CTP_EUNSUPPORTED
-    assert _bwd_bwd(capi, _prob(capi, channels=513), args) == capi.CTP_EUNSUPPORTED
+    assert _bwd_bwd(capi, _prob(capi, channels=1025), args) == capi.CTP_EUNSUPPORTED
     assert len(args) == len(capi.lib().conv_tp_bwd_bwd.argtypes) - 2
     for k in range(16):
         a = list(args)

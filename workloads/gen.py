@@ -29,7 +29,8 @@ from __future__ import annotations
 
 import numpy as np
 
-# (l_in, l_sh, l_out) are equal in every workload below.
+# (l_in, l_sh, l_out) are equal in the named workloads below; poisson_degrees
+# draws small graphs with independent degrees.
 TINY = dict(name="tiny", n_nodes=64, channels=16, lmax=1, deg=16)
 L2_FWD = dict(name="l2fwd", n_nodes=32768, channels=128, lmax=2, mean_deg=45.0)
 L3_FB = dict(name="l3fb", n_nodes=16384, channels=128, lmax=3, mean_deg=45.0)
@@ -162,6 +163,24 @@ def poisson_small(n_nodes: int, channels: int, lmax: int, mean_deg: float = 45.0
     return dict(name=f"poisson_n{n_nodes}_c{channels}_l{lmax}", n_nodes=n_nodes,
                 n_edges=e, channels=channels, lmax=lmax, row_ptr=row_ptr,
                 senders=senders, vec=vec, x=x, w=w, grad_out=g)
+
+
+def poisson_degrees(n_nodes: int, channels: int, l_in: int, l_sh: int, n_paths: int, out_dim: int,
+                    mean_deg: float = 12.0, seed: int = 0):
+    """Small Poisson workload with independent degrees: x [N][(l_in+1)^2][C],
+    vec [E][3] (the caller evaluates Y up to l_sh), w [E][n_paths][C] and
+    grad_out [N][out_dim][C].  The path count and output width are passed in
+    (they belong to the oracle and the library), so this draws only shapes."""
+    rng = rng_for(seed)
+    row_ptr, senders = poisson_graph(n_nodes, mean_deg, rng)
+    e = senders.size
+    vec = unit_vectors(e, rng)
+    x = normal((n_nodes, (l_in + 1) ** 2, channels), rng)
+    w = normal((e, n_paths, channels), rng)
+    g = normal((n_nodes, out_dim, channels), rng)
+    return dict(name=f"poisson_n{n_nodes}_c{channels}_deg{l_in}{l_sh}", n_nodes=n_nodes, n_edges=e,
+                channels=channels, lmax=None, l_sh=l_sh, row_ptr=row_ptr, senders=senders, vec=vec, x=x, w=w,
+                grad_out=g)
 
 
 def poisson_full(n_nodes: int, channels: int, lmax: int, device, mean_deg: float = 45.0,
