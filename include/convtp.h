@@ -193,6 +193,23 @@ int32_t conv_tp_bwd_msg(const conv_tp_problem *prob, const float *grad_out, cons
                         const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw,
                         float *dy_or_dvec, float *workspace, int64_t workspace_bytes, void *stream);
 
+/* conv_tp_bwd_msg for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, outputs and kernels without the workspace arguments.
+ * The edge messages go to a fixed scratch array of 256 MiB (268435456 bytes)
+ * that the library holds on each device it runs on until the process ends; the
+ * call itself allocates nothing.  Problems whose messages need more,
+ * E * (l_in+1)^2 * C * 4 bytes > 268435456 (conv_tp_bwd_msg_workspace), are
+ * rejected with CTP_EUNSUPPORTED before any HIP call.  The first call on a
+ * device looks up that device's scratch address (hipGetSymbolAddress).
+ * Calls on one device share the scratch, so calls that overlap on one device
+ * (different streams or threads without ordering) race and give undefined
+ * results; calls on one stream are ordered and safe. */
+int32_t conv_tp_bwd_msg_noalloc(const conv_tp_problem *prob, const float *grad_out, const float *x,
+                                const float *y_or_vec, const float *w, const int32_t *row_ptr,
+                                const int32_t *senders, const int32_t *send_ptr, const int32_t *send_perm,
+                                const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec, void *stream);
+
 /* VJP of the backward (the "VJP-of-VJP" of FlashCart's section on symbolic
  * VJPs, needed to train on forces), Y given.  With cotangents a_x, a_w, a_y of
  * conv_tp_bwd's outputs (dx, dw, dY) and L2 = <a_x, dx> + <a_w, dw> + <a_y, dY>,
@@ -297,7 +314,7 @@ const char *conv_tp_last_error(void);
 /* ABI version (major * 100 + minor): 101 added conv_tp_problem.variant, 102
  * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward), 104 conv_tp_bwd_dy, 105
  * independent degrees, up to 1024 channels in every backward and variant 1
- * in conv_tp_bwd_bwd. */
+ * in conv_tp_bwd_bwd, 106 conv_tp_bwd_msg_noalloc. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

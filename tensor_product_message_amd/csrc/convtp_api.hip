@@ -142,6 +142,37 @@ int64_t msg_workspace_bytes(const Shape& s) { return s.E * s.D1 * s.C * (int64_t
 std::mutex g_bad_mu;
 std::unordered_map<int, unsigned long long*> g_bad_buf;   // per-device counter for conv_tp_check_graph
 
+// Edge-message workspace of conv_tp_bwd_msg_noalloc: a file-scope device
+// array, so that call allocates nothing.  Every device the library runs on
+// holds its own copy (at its own address) until the process ends.  Its host
+// name is only a stand-in for the symbol: host code uses the per-device
+// address from hipGetSymbolAddress, never `scratch` itself.
+constexpr int64_t kNoAllocScratchBytes = int64_t(256) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, float*> g_scratch_ptr;   // device id -> address of that device's `scratch`
+
+// Address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept.
+int scratch_on_current_device(float** out) {
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *out = it->second;
+        return CTP_OK;
+    }
+    float* ptr = nullptr;
+    if (hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)); e != hipSuccess)
+        return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(CTP_EHIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = ptr;
+    *out = ptr;
+    return CTP_OK;
+}
+
 }  // namespace
 
 namespace ctp {
@@ -177,7 +208,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 105; }
+int32_t conv_tp_version(void) { return 106; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
@@ -300,6 +331,29 @@ int32_t conv_tp_bwd_msg(const conv_tp_problem* prob, const float* grad_out, cons
                     (long long)need_bytes);
     if (int r = need(workspace, s.E * s.D1 * s.C, 16, "workspace")) return r;
     return hip_status(ctp::launch_bwd_msg(a, workspace, static_cast<hipStream_t>(stream)), "conv_tp_bwd_msg launch");
+}
+
+int32_t conv_tp_bwd_msg_noalloc(const conv_tp_problem* prob, const float* grad_out, const float* x,
+                                const float* y_or_vec, const float* w, const int32_t* row_ptr,
+                                const int32_t* senders, const int32_t* send_ptr, const int32_t* send_perm,
+                                const int32_t* send_recv, float* dx, float* dw, float* dy_or_dvec, void* stream) {
+    Shape s{};
+    ctp::LaunchArgs a{};
+    if (int r = bwd_args(prob, grad_out, x, y_or_vec, w, row_ptr, senders, send_ptr, send_perm, send_recv, dx, dw,
+                         dy_or_dvec, &s, &a))
+        return r;
+    const int64_t need_bytes = msg_workspace_bytes(s);
+    if (need_bytes > kNoAllocScratchBytes)
+        return fail(CTP_EUNSUPPORTED,
+                    "conv_tp_bwd_msg_noalloc: the edge messages need %lld bytes (E * (l_in+1)^2 * C * 4), above its "
+                    "fixed scratch of %lld bytes; call conv_tp_bwd_msg with a workspace instead",
+                    (long long)need_bytes, (long long)kNoAllocScratchBytes);
+    if (prob->n_nodes == 0) return ok();
+    float* ws = nullptr;
+    if (int r = scratch_on_current_device(&ws)) return r;
+    // pass 1 writes every message row before pass 2 reads it: nothing to clear
+    return hip_status(ctp::launch_bwd_msg(a, ws, static_cast<hipStream_t>(stream)),
+                      "conv_tp_bwd_msg_noalloc launch");
 }
 
 int32_t conv_tp_bwd_bwd(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* y,

@@ -258,6 +258,26 @@ def conv_tp_bwd_msg(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: i
     return dx, dw, dy
 
 
+def conv_tp_bwd_msg_noalloc(grad_out, x, y_or_vec, w, graph: Graph, lmax, y_mode: int = Y_GIVEN,
+                            dx=None, dw=None, dy=None, variant: int = SUMMED):
+    """conv_tp_bwd_msg with the library's fixed per-device scratch instead of a
+    workspace (see include/convtp.h; rejects problems whose messages exceed it)."""
+    n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant)
+    _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
+    send_ptr, send_perm, send_recv = graph.transpose
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w) if dw is None else dw
+    dy = torch.empty_like(y_or_vec) if dy is None else dy
+    _want(dx, "dx", x.shape, device=x.device)
+    _want(dw, "dw", w.shape, device=x.device)
+    _want(dy, "dy", y_or_vec.shape, device=x.device)
+    prob = _problem(n, e, c, lmax, y_mode, ALGO_CSR, variant)
+    check(lib().conv_tp_bwd_msg_noalloc(ctypes.byref(prob), _p(grad_out), _p(x), _p(y_or_vec), _p(w),
+                                        _p(graph.row_ptr), _p(graph.senders), _p(send_ptr), _p(send_perm),
+                                        _p(send_recv), _p(dx), _p(dw), _p(dy), _stream(x)))
+    return dx, dw, dy
+
+
 def conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph: Graph, lmax, out=None, variant: int = SUMMED):
     """VJP of conv_tp_bwd (Y given): gradients (g_x, g_w, g_y, g_grad) of
     <a_x, dx> + <a_w, dw> + <a_y, dY> (see include/convtp.h)."""

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 105
+    assert L.conv_tp_version() == 106
 
 
 def test_paths_match_oracle(capi):
@@ -183,6 +183,25 @@ def test_bwd_msg_rejections(capi):
     assert "workspace" in L.conv_tp_last_error().decode()
     assert _bwd_msg(capi, p, ws=NUL, nbytes=nb.value) == capi.CTP_EINVAL
     assert _bwd_msg(capi, p, ws=MIS, nbytes=nb.value) == capi.CTP_EALIGN
+
+
+def test_bwd_msg_noalloc_rejections(capi):
+    # same argument checks as conv_tp_bwd_msg, then a size check against the
+    # fixed scratch, all before any HIP call
+    L = capi.lib()
+    f = lambda p, **kw: L.conv_tp_bwd_msg_noalloc(ctypes.byref(p), *dict(  # noqa: E731
+        dict(g=A, x=A, y=A, w=A, rp=A, s=A, sp=A, pe=A, sr=A, dx=A2, dw=A2, dy=A2), **kw).values(), NUL)
+    assert len(L.conv_tp_bwd_msg_noalloc.argtypes) == 14
+    assert f(_prob(capi, algo=1)) == capi.CTP_EUNSUPPORTED
+    assert f(_prob(capi, channels=1025)) == capi.CTP_EUNSUPPORTED
+    for k in ("g", "x", "y", "w", "rp", "s", "sp", "pe", "sr", "dx", "dw", "dy"):
+        assert f(_prob(capi), **{k: NUL}) == capi.CTP_EINVAL, k
+    # E * (l_in+1)^2 * C * 4 = 32769 * 16 * 128 * 4 > 256 MiB
+    big = _prob(capi, n_nodes=100, n_edges=32769, channels=128, l_in=3, l_sh=3, l_out=3)
+    assert f(big) == capi.CTP_EUNSUPPORTED
+    assert "scratch" in L.conv_tp_last_error().decode()
+    assert f(_empty(capi, channels=1024, l_in=3, l_sh=3, l_out=3), g=NUL, x=NUL, y=NUL, w=NUL, s=NUL, pe=NUL,
+             sr=NUL, dx=NUL, dw=NUL, dy=NUL) == capi.CTP_OK
 
 
 def test_bwd_dy_rejections(capi):
