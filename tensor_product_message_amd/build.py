@@ -70,9 +70,14 @@ def build(verbose: bool = True, incremental: bool = False, workers: int = None) 
     jobs = _jobs(objdir)
     todo = jobs
     if incremental:
-        newest = max(os.path.getmtime(p) for p in glob.glob(os.path.join(CSRC, "*"))
-                     + glob.glob(os.path.join(HERE, "..", "include", "*.h")))
-        todo = [j for j in jobs if not os.path.exists(j[1]) or os.path.getmtime(j[1]) < newest]
+        headers = glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(HERE, "..", "include", "*.h"))
+        newest_header = max(os.path.getmtime(p) for p in headers)
+
+        def stale(job):
+            src, obj, _ = job
+            newest = max(newest_header, os.path.getmtime(os.path.join(CSRC, src)))
+            return not os.path.exists(obj) or os.path.getmtime(obj) < newest
+        todo = [j for j in jobs if stale(j)]
     n = workers or min(16, os.cpu_count() or 8)
     with ThreadPoolExecutor(max_workers=n) as ex:
         list(ex.map(_compile, todo))

@@ -8,7 +8,8 @@
 //   2. inclusive scan of send_ptr[0..N], so send_ptr[s + 1] = first slot of s;
 //   3. place every edge with an atomic cursor on send_ptr[s + 1], which leaves
 //      send_ptr[s + 1] = one past the last slot of s, i.e. the final pointers;
-//   4. sort each sender's segment ascending (restores CSR order exactly);
+//   4. sort each sender's segment ascending (restores CSR order exactly; a
+//      bitonic network per sender, one workgroup each);
 //   5. send_recv[k] = receiver of send_perm[k] by binary search in row_ptr.
 // Integer atomics make steps 1-3 order-independent in result after step 4, so
 // the output is bit-exact and identical from run to run.
@@ -72,22 +73,63 @@ __global__ void k_place(int n_nodes, int n_edges, const int32_t* __restrict__ se
     }
 }
 
-// One thread per sender: insertion sort of its segment (segments are short;
-// the keys are distinct edge ids, so the sorted order is unique).
-__global__ void k_sort_segments(int n_nodes, const int32_t* __restrict__ send_ptr, int32_t* __restrict__ send_perm) {
-    long s = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long stride = (long)gridDim.x * blockDim.x;
-    for (; s < n_nodes; s += stride) {
-        const int b = send_ptr[s], e = send_ptr[s + 1];
-        for (int k = b + 1; k < e; ++k) {
-            const int32_t v = send_perm[k];
-            int q = k - 1;
-            while (q >= b && send_perm[q] > v) {
-                send_perm[q + 1] = send_perm[q];
-                --q;
-            }
-            send_perm[q + 1] = v;
+// One workgroup per sender sorts its segment ascending (the keys are
+// distinct edge ids, so the sorted order is unique) with a bitonic network:
+// O(n log^2 n) work, O(log^2 n) barrier-separated stages.  Segments up to
+// kSortLds elements are sorted in LDS, padded to a power of two with INT_MAX;
+// longer ones (hubs) in place in global memory, where every comparator puts
+// the smaller key at the lower index and comparators that reach past the
+// segment's end are skipped (the missing elements act as +infinity and would
+// stay in place), so no padding is needed.
+constexpr int kSortThreads = 256;
+constexpr int kSortLds = 4096;
+
+__device__ __forceinline__ void cmp_swap(int32_t* a, int i, int j) {
+    const int32_t x = a[i], y = a[j];
+    if (y < x) {
+        a[i] = y;
+        a[j] = x;
+    }
+}
+
+// Bitonic sort of a[0..n) (n <= m, m a power of two) by the "flip" network:
+// in merge stage k the first comparator of each block of size k pairs i with
+// its mirror image, the later ones pair i with i + j.
+__device__ void bitonic_sort(int32_t* a, int n, int m, int tid, int nth) {
+    for (int k = 2; k <= m; k <<= 1) {
+        for (int t = tid; t < m / 2; t += nth) {
+            const int blk = t / (k / 2), off = t % (k / 2);
+            const int i = blk * k + off, j = blk * k + k - 1 - off;
+            if (j < n) cmp_swap(a, i, j);
         }
+        __syncthreads();
+        for (int j2 = k / 4; j2 >= 1; j2 >>= 1) {
+            for (int t = tid; t < m / 2; t += nth) {
+                const int blk = t / j2, off = t % j2;
+                const int i = blk * 2 * j2 + off, j = i + j2;
+                if (j < n) cmp_swap(a, i, j);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kSortThreads)
+k_sort_segments(const int32_t* __restrict__ send_ptr, int32_t* __restrict__ send_perm) {
+    __shared__ int32_t buf[kSortLds];
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int b = send_ptr[s], n = send_ptr[s + 1] - b;
+    if (n < 2) return;
+    int m = 2;
+    while (m < n) m <<= 1;
+    if (m <= kSortLds) {
+        for (int t = tid; t < m; t += kSortThreads) buf[t] = t < n ? send_perm[b + t] : 0x7fffffff;
+        __syncthreads();
+        bitonic_sort(buf, m, m, tid, kSortThreads);
+        for (int t = tid; t < n; t += kSortThreads) send_perm[b + t] = buf[t];
+    } else {
+        // the workgroup's writes to global memory are visible to it after each barrier
+        bitonic_sort(send_perm + b, n, m, tid, kSortThreads);
     }
 }
 
@@ -137,8 +179,7 @@ hipError_t launch_transpose(int n_nodes, int n_edges, const int32_t* row_ptr, co
         hipLaunchKernelGGL(k_place, dim3(grid_for(n_edges, 256)), dim3(256), 0, st, n_nodes, n_edges, senders,
                            send_ptr, send_perm);
         if (n_nodes > 0)
-            hipLaunchKernelGGL(k_sort_segments, dim3(grid_for(n_nodes, 64)), dim3(64), 0, st, n_nodes, send_ptr,
-                               send_perm);
+            hipLaunchKernelGGL(k_sort_segments, dim3(n_nodes), dim3(kSortThreads), 0, st, send_ptr, send_perm);
         hipLaunchKernelGGL(k_recv_of, dim3(grid_for(n_edges, 256)), dim3(256), 0, st, n_nodes, n_edges, row_ptr,
                            send_perm, send_recv);
     }

@@ -277,7 +277,7 @@ def test_random_shapes_every_entry_point(ctp, dev):
 # ------------------------------------------------------------ bookkeeping and harmonics
 
 
-@pytest.mark.parametrize("which", ["tiny", "poisson", "water", "skewed"])
+@pytest.mark.parametrize("which", ["tiny", "poisson", "water", "skewed", "hubs"])
 def test_transpose_bit_exact(ctp, dev, which):
     if which == "tiny":
         d = gen.tiny()
@@ -294,6 +294,20 @@ def test_transpose_bit_exact(ctp, dev, which):
         recv = np.sort(rng.integers(0, n, size=4000))
         s = rng.integers(0, n, size=4000).astype(np.int32)
         s[rng.choice(4000, 3000, replace=False)] = 7
+        rp = og.row_ptr_from_receivers(recv, n)
+    if which == "hubs":
+        # segments above the in-LDS sort size: one sender with 50,000 out-edges,
+        # one with 4097 (just above 4096) and one with exactly 4096
+        n = 3000
+        rng = np.random.default_rng(12)
+        e = 70000
+        recv = np.sort(rng.integers(0, n, size=e))
+        s = rng.integers(0, n, size=e).astype(np.int32)
+        pick = rng.permutation(e)
+        s[pick[:50000]] = 11
+        s[pick[50000:54097]] = 12
+        s[pick[54097:58193]] = 13
+        s[pick[58193:]] = rng.integers(14, n, size=e - 58193)
         rp = og.row_ptr_from_receivers(recv, n)
     ref = og.transpose(n, rp, s)
     got = ctp.build_transpose(n, T(rp, dev), T(s, dev))
