@@ -27,7 +27,8 @@ from . import cg as _cg
 from . import graph as _graph
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of the C loop (the sanitizer test's)
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "convtp_oracle.c")
 
 

@@ -9,7 +9,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libconvtp.so")
+# the in-tree build; CONVTP_LIB names another build of the same library (the
+# sanitizer test loads an AddressSanitizer build of the C ABI front this way)
+LIB_PATH = os.environ.get("CONVTP_LIB") or os.path.join(HERE, "libconvtp.so")
 
 CTP_OK, CTP_EINVAL, CTP_EUNSUPPORTED, CTP_EALIGN, CTP_EHIP, CTP_EGRAPH = range(6)
 STATUS_NAMES = {0: "CTP_OK", 1: "CTP_EINVAL", 2: "CTP_EUNSUPPORTED", 3: "CTP_EALIGN",
