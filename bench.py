@@ -156,7 +156,7 @@ def workload_l3fb(ctp, torch, dev, args):
 
     def step(t):
         t.run("fwd", lambda: ctp.conv_tp_fwd(x, y, w, g, L, y_mode, fwd_algo, out=out))
-        t.run("bwd", lambda: ctp.conv_tp_bwd(G, x, y, w, g, L, y_mode, dx=dx, dw=dw, dy=dy))
+        t.run("bwd", lambda: ctp.conv_tp_bwd(G, x, y, w, g, L, y_mode, dx=dx, dw=dw, dy=dy, algo=fwd_algo))
 
     kb = {"fwd": fwd_bytes(*shp), "bwd": bwd_bytes(*shp)}
     ffma, bfma = fma_per_edge_channel(ctp, L)
@@ -165,7 +165,7 @@ def workload_l3fb(ctp, torch, dev, args):
                        f"Poisson(45) in-degree, {'vec' if args.vec else 'Y'} given, fp32",
            "n_nodes": shp[0], "n_edges": shp[1], "channels": 128, "lmax": 3,
            "y_mode": "vec" if args.vec else "Y", "paths": shp[6],
-           "forward": "edge frame (algo 2)" if args.frame else "direct (algo 0)"}
+           "algo": "edge frame (algo 2), forward and backward" if args.frame else "direct (algo 0)"}
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=shp[1], cfg=cfg,
                 cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=True))
 
@@ -350,8 +350,8 @@ def workload_water(ctp, torch, dev, args):
     def step(t):
         t.run("fwd1", lambda: ctp.conv_tp_fwd(x0, v, w1, g, L, y_mode, fwd_algo, out=h1))
         t.run("fwd2", lambda: ctp.conv_tp_fwd(h1, v, w2, g, L, y_mode, fwd_algo, out=h2))
-        t.run("bwd2", lambda: ctp.conv_tp_bwd(G, h1, v, w2, g, L, y_mode, dx=dh1, dw=dw2, dy=dv2))
-        t.run("bwd1", lambda: ctp.conv_tp_bwd(dh1, x0, v, w1, g, L, y_mode, dx=dx0, dw=dw1, dy=dv1))
+        t.run("bwd2", lambda: ctp.conv_tp_bwd(G, h1, v, w2, g, L, y_mode, dx=dh1, dw=dw2, dy=dv2, algo=fwd_algo))
+        t.run("bwd1", lambda: ctp.conv_tp_bwd(dh1, x0, v, w1, g, L, y_mode, dx=dx0, dw=dw1, dy=dv1, algo=fwd_algo))
 
     E = wb["n_edges"]
     shp = (n, E, 128, 16, 16, 16, ctp.num_paths(L), 3)
@@ -359,7 +359,7 @@ def workload_water(ctp, torch, dev, args):
     cfg = {"workload": f"water-box-shaped step: 1503 atoms, {E} edges (10% zero-weight padding), "
                        "C=128, lmax=3, vec given, two layers forward + backward to edge vectors, fp32",
            "n_nodes": n, "n_edges": E, "channels": 128, "lmax": 3, "layers": 2,
-           "forward": "edge frame (algo 2)" if args.frame else "direct (algo 0)"}
+           "algo": "edge frame (algo 2), forward and backward" if args.frame else "direct (algo 0)"}
     return dict(step=step, kernel_bytes=kb, dominant="bwd1", edges=E, cfg=cfg, cpu=None)
 
 
@@ -466,10 +466,25 @@ def workload_hbm(ctp, torch, dev, args):
                 edges=0, cfg={"workload": "HBM stream probes: 2 GiB fp32 read, write and copy"}, cpu=None)
 
 
+def workload_valu(ctp, torch, dev, args):
+    """Arithmetic ceiling: the library's fp32 FMA probe (non-packed, eight
+    chains per lane, eight waves per SIMD on every CU)."""
+    sink = torch.zeros(4, device=dev)
+    iters = 20000
+    fmas = ctp.valu_probe(iters, sink)   # one launch; the library reports the FMAs it performs
+
+    def step(t):
+        t.run("valu", lambda: ctp.valu_probe(iters, sink))
+
+    return dict(step=step, kernel_bytes={}, kernel_flops={"valu": 2.0 * fmas}, dominant="valu", edges=0,
+                cfg={"workload": "VALU probe: non-packed fp32 FMA, 8 chains per lane, 2048 x 256 threads"},
+                cpu=None, flops_metric=True)
+
+
 WORKLOADS = {"l3fb": workload_l3fb, "l2fwd": workload_l2fwd, "sweepC": workload_sweep,
              "water": workload_water, "tiny": workload_tiny, "copy": workload_copy, "hbm": workload_hbm,
              "node3": workload_node, "l3dd": workload_l3dd, "l3mace": workload_l3mace,
-             "gather": workload_gather, "l3ddvec": workload_l3ddvec}
+             "gather": workload_gather, "l3ddvec": workload_l3ddvec, "valu": workload_valu}
 
 
 # ------------------------------------------------------------ CPU baseline (oracle)
@@ -553,7 +568,7 @@ def main():
     ap.add_argument("--gather-nodes", type=int, default=64, help="gather only: nodes the row gathers touch")
     ap.add_argument("--vec", action="store_true", help="l3fb with edge vectors instead of Y")
     ap.add_argument("--frame", action="store_true",
-                    help="l3fb --vec and water: the forward in each edge's frame (algo 2)")
+                    help="l3fb --vec and water: forward and backward in each edge's frame (algo 2)")
     ap.add_argument("--bwd", choices=("msg", "sender"), default="msg",
                     help="l3mace: backward through edge messages (conv_tp_bwd_msg) or sender-major (conv_tp_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -587,6 +602,18 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = s0.elapsed_time(s1) / args.steps
 
+    if wl.get("flops_metric"):
+        k = wl["dominant"]
+        tf = wl["kernel_flops"][k] / (timer.mean_ms(k) * 1e-3) / 1e12
+        print(json.dumps({"metric": "fp32 VALU FMA rate (measurement probe)", "value": round(tf, 2),
+                          "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+                          "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": wl["cfg"],
+                          "roofline": {"bound": "alu", "kernel": k, "achieved": round(tf, 2),
+                                       "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(tf / VALU_PEAK_TFLOPS, 4), "traffic": None},
+                          "cpu_baseline": None}), flush=True)
+        return
     value_kernels = wl.get("value_kernels", tuple(wl["kernel_bytes"]))
     step_bytes = sum(wl["kernel_bytes"][k] for k in value_kernels)
     if value_kernels != tuple(wl["kernel_bytes"]):

@@ -82,8 +82,9 @@ extern "C" {
 enum {
     CTP_OK = 0,
     CTP_EINVAL = 1,        /* null pointer, negative size, bad enum value */
-    CTP_EUNSUPPORTED = 2,  /* degree outside 0..3, channels above 1024, algo 1 or 2 in a backward,
-                              algo 2 with Y given or variant 1, edge vectors where only Y is taken */
+    CTP_EUNSUPPORTED = 2,  /* degree outside 0..3, channels above 1024, algo 1 in a backward, algo 2
+                              with Y given, variant 1 or in an entry point other than conv_tp_fwd and
+                              conv_tp_bwd, edge vectors where only Y is taken */
     CTP_EALIGN = 3,        /* a feature/weight array not 16-byte aligned, an index array not 4-byte aligned */
     CTP_EHIP = 4,          /* HIP launch or runtime error (message from hipGetErrorString) */
     CTP_EGRAPH = 5         /* graph arguments inconsistent (e.g. edges without nodes) */
@@ -98,7 +99,7 @@ typedef struct conv_tp_problem {
     int32_t l_out;     /* max degree of out, 0..3 (independent of l_in and l_sh) */
     int32_t y_mode;    /* 0: Y[E][D_sh] given; 1: vec[E][3] given, Y evaluated in-kernel */
     int32_t algo;      /* 0: CSR segmented sum, deterministic; 1: edge-parallel atomics (forward only);
-                          2: CSR in each edge's own frame (forward only, y_mode 1, variant 0) */
+                          2: in each edge's own frame (conv_tp_fwd and conv_tp_bwd; y_mode 1, variant 0) */
     int32_t variant;   /* 0: every triangle path, same-l3 paths summed into one block of D_out = (l_out+1)^2;
                           1: MACE's convolution - natural-parity paths only (l1+l2+l3 even; e3j Table 3's
                           MACE model, FlashCart's admissible-coupling section), each path with an output
@@ -148,7 +149,14 @@ int32_t conv_tp_fwd(const conv_tp_problem *prob, const float *x, const float *y_
  * and channel tile walks the sender's out-edges through (send_ptr, send_perm,
  * send_recv), one channel per lane; dY is summed over the tile's channels in a
  * fixed order (up to 512 channels in one tile; two tiles above that, see
- * Determinism).  algo must be 0; C up to 1024. */
+ * Determinism).  C up to 1024.
+ * algo 0: direct.  algo 2 (edge vectors, variant 0): in each edge's frame, as
+ * the algo 2 forward: x and grad_out are rotated so that the edge points along
+ * z, coupled through the m2 = 0 slice of every path, dx rotated back, and of
+ * the harmonic gradient only the m2 = +-1 components (the ones with a gradient
+ * across the edge direction there) are formed for dvec.  The same result up
+ * to rounding, about 45% fewer FMAs per edge and channel at l = 3.  algo 1 is
+ * rejected (CTP_EUNSUPPORTED). */
 int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y_or_vec,
                     const float *w, const int32_t *row_ptr, const int32_t *senders, const int32_t *send_ptr,
                     const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec,
@@ -308,13 +316,23 @@ int32_t conv_tp_node_bwd(const conv_tp_node_problem *prob, const float *grad_out
  * pointers.  Enqueued on `stream`. */
 int32_t conv_tp_stream_probe(int32_t kind, const float *src, float *dst, int64_t n_floats, void *stream);
 
+/* Measurement helper, not part of the operation: an fp32 FMA kernel without
+ * packed instructions (the build of every kernel here excludes them), eight
+ * independent chains per lane, enough workgroups for eight waves per SIMD on
+ * every CU.  *fmas (host) receives the number of FMAs one launch performs;
+ * timing the launch gives the FMA rate the vector ALUs sustain, against
+ * which arithmetic-bound kernels are read.  dst (device, >= 1 float, 4-byte
+ * aligned) receives a value only for a non-finite result.  iterations >= 0. */
+int32_t conv_tp_valu_probe(int64_t iterations, float *dst, int64_t *fmas, void *stream);
+
 /* Message for the last non-zero status on this thread ("" if none). */
 const char *conv_tp_last_error(void);
 
 /* ABI version (major * 100 + minor): 101 added conv_tp_problem.variant, 102
  * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward), 104 conv_tp_bwd_dy, 105
  * independent degrees, up to 1024 channels in every backward and variant 1
- * in conv_tp_bwd_bwd, 106 conv_tp_bwd_msg_noalloc. */
+ * in conv_tp_bwd_bwd, 106 conv_tp_bwd_msg_noalloc, 107 conv_tp_valu_probe and algo 2 in
+ * conv_tp_bwd. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

@@ -9,4 +9,4 @@ from .ops import (SLOTS, SUMMED, layout, out_dim, degrees, ConvTPBackward, ConvT
                   conv_tp_bwd_bwd_vec, spherical_harmonics_jvp, spherical_harmonics_bwd_bwd,
                   conv_tp_fwd, coupling, dim, node_tp_bwd, node_tp_fwd, num_paths, paths,
                   spherical_harmonics,
-                  spherical_harmonics_backward, stream_probe)
+                  spherical_harmonics_backward, stream_probe, valu_probe)

@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "CTP_OK", 1: "CTP_EINVAL", 2: "CTP_EUNSUPPORTED", 3: "CTP_EAL
 EXPORTS = ("conv_tp_num_paths", "conv_tp_paths", "conv_tp_layout", "conv_tp_coupling", "conv_tp_fwd", "conv_tp_bwd",
            "conv_tp_bwd_msg_workspace", "conv_tp_bwd_msg", "conv_tp_bwd_msg_noalloc", "conv_tp_bwd_dy", "conv_tp_bwd_bwd",
            "conv_tp_sh", "conv_tp_sh_bwd", "conv_tp_build_transpose", "conv_tp_check_graph",
-           "conv_tp_sh_jvp", "conv_tp_sh_bwd_bwd", "conv_tp_node_fwd", "conv_tp_node_bwd", "conv_tp_stream_probe", "conv_tp_last_error",
+           "conv_tp_sh_jvp", "conv_tp_sh_bwd_bwd", "conv_tp_node_fwd", "conv_tp_node_bwd", "conv_tp_stream_probe", "conv_tp_valu_probe", "conv_tp_last_error",
            "conv_tp_version")
 
 
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "conv_tp_build_transpose": ([i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "conv_tp_check_graph": ([i32, i32, vp, vp, i64p, vp], i32),
         "conv_tp_stream_probe": ([i32, vp, vp, ctypes.c_int64, vp], i32),
+        "conv_tp_valu_probe": ([ctypes.c_int64, vp, i64p, vp], i32),
         "conv_tp_node_fwd": ([npp, vp, vp, vp, vp, vp], i32),
         "conv_tp_node_bwd": ([npp] + [vp] * 8, i32),
         "conv_tp_last_error": ([], ctypes.c_char_p),

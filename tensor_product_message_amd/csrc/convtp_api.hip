@@ -107,7 +107,9 @@ int bwd_args(const conv_tp_problem* prob, const float* grad_out, const float* x,
              ctp::LaunchArgs* out) {
     Shape& s = *sp;
     if (int r = check_problem(prob, &s)) return r;
-    if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the backward has only the deterministic algorithm (algo 0)");
+    if (prob->algo == 1) return fail(CTP_EUNSUPPORTED, "the backward has no atomic variant (algo 1)");
+    if (prob->algo == 2 && (prob->y_mode != 1 || prob->variant != ctp::kVariantSummed))
+        return fail(CTP_EUNSUPPORTED, "algo 2 (edge frame) needs edge vectors (y_mode 1) and variant 0");
     if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
     if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
     if (int r = need(y_or_vec, s.E * s.S, 4, "y_or_vec")) return r;
@@ -208,7 +210,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 106; }
+int32_t conv_tp_version(void) { return 107; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
@@ -325,6 +327,7 @@ int32_t conv_tp_bwd_msg(const conv_tp_problem* prob, const float* grad_out, cons
     if (int r = bwd_args(prob, grad_out, x, y_or_vec, w, row_ptr, senders, send_ptr, send_perm, send_recv, dx, dw,
                          dy_or_dvec, &s, &a))
         return r;
+    if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_msg has only the direct algorithm (algo 0)");
     const int64_t need_bytes = msg_workspace_bytes(s);
     if (workspace_bytes < need_bytes)
         return fail(CTP_EINVAL, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
@@ -342,6 +345,8 @@ int32_t conv_tp_bwd_msg_noalloc(const conv_tp_problem* prob, const float* grad_o
     if (int r = bwd_args(prob, grad_out, x, y_or_vec, w, row_ptr, senders, send_ptr, send_perm, send_recv, dx, dw,
                          dy_or_dvec, &s, &a))
         return r;
+    if (prob->algo != 0)
+        return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_msg_noalloc has only the direct algorithm (algo 0)");
     const int64_t need_bytes = msg_workspace_bytes(s);
     if (need_bytes > kNoAllocScratchBytes)
         return fail(CTP_EUNSUPPORTED,
@@ -526,6 +531,15 @@ int32_t conv_tp_stream_probe(int32_t kind, const float* src, float* dst, int64_t
     if (n_floats == 0) return ok();
     return hip_status(ctp::launch_stream_probe(kind, src, dst, (long)n_floats, static_cast<hipStream_t>(stream)),
                       "stream probe launch");
+}
+
+int32_t conv_tp_valu_probe(int64_t iterations, float* dst, int64_t* fmas, void* stream) {
+    if (iterations < 0) return fail(CTP_EINVAL, "iterations = %lld must be >= 0", (long long)iterations);
+    if (fmas == nullptr) return fail(CTP_EINVAL, "fmas is null");
+    if (int r = need(dst, 1, 4, "dst")) return r;
+    *fmas = ctp::valu_probe_fmas(iterations);
+    if (iterations == 0) return ok();
+    return hip_status(ctp::launch_valu_probe(iterations, dst, static_cast<hipStream_t>(stream)), "valu probe launch");
 }
 
 int32_t conv_tp_check_graph(int32_t n_nodes, int32_t n_edges, const int32_t* row_ptr, const int32_t* senders,

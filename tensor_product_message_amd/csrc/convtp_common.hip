@@ -220,6 +220,9 @@ hipError_t launch_fwd(const LaunchArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st) {
     if (a.n_nodes == 0) return hipSuccess;
+    if (a.algo == 2)
+        return by_triple(triple_key(a.l_in, a.l_sh, a.l_out),
+                         [&]<int A, int B, int C>() { return Triple<A, B, C>::bwd_frame(a, st); });
     return by_triple(triple_key(a.l_in, a.l_sh, a.l_out),
                      [&]<int A, int B, int C>() { return Triple<A, B, C>::bwd(a, st); });
 }

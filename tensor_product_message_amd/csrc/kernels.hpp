@@ -10,7 +10,7 @@ namespace ctp {
 struct LaunchArgs {
     int l_in, l_sh, l_out; // degrees of x, Y and out
     int n_nodes, n_edges, C;
-    int algo;              // 0: CSR deterministic, 1: edge-parallel atomic, 2: edge frame (forward only)
+    int algo;              // 0: CSR deterministic, 1: edge-parallel atomic (forward), 2: edge frame (edge vectors)
     int vec_mode;          // 0: Y[E][D2] given, 1: vec[E][3] given
     int variant;           // 0: all paths, same-l3 sums; 1: natural-parity paths, one output slot each
     const float* x;        // [N][D1][C]
@@ -52,6 +52,7 @@ struct Triple {
     static hipError_t fwd(const LaunchArgs& a, hipStream_t st);          // algo 0 and 1
     static hipError_t fwd_frame(const LaunchArgs& a, hipStream_t st);    // algo 2, variant 0
     static hipError_t bwd(const LaunchArgs& a, hipStream_t st);          // sender-major
+    static hipError_t bwd_frame(const LaunchArgs& a, hipStream_t st);    // algo 2, edge vectors, variant 0
     static hipError_t bwd_recv(const LaunchArgs& a, float* msg, hipStream_t st);   // message pass 1
     static hipError_t bwd_dy(const LaunchArgs& a, hipStream_t st);
     static hipError_t double_bwd(const DoubleArgs& a, hipStream_t st);
@@ -81,6 +82,8 @@ hipError_t launch_node_fwd(int L, int n_nodes, int C, const float* x, const floa
 hipError_t launch_node_bwd(int L, int n_nodes, int C, const float* G, const float* x, const float* y,
                            const float* w, float* dx, float* dy, float* dw, hipStream_t st);
 hipError_t launch_stream_probe(int kind, const float* src, float* dst, long n_floats, hipStream_t st);
+hipError_t launch_valu_probe(long iters, float* dst, hipStream_t st);
+long valu_probe_fmas(long iters);
 hipError_t launch_check_graph(int n_nodes, int n_edges, const int32_t* row_ptr, const int32_t* senders,
                               unsigned long long* d_bad, hipStream_t st);
 

@@ -3,7 +3,9 @@
 // grid-stride loop (4096 workgroups for reads, 16384 for writes and copies,
 // the best of a sweep on MI355X).  They give the bandwidth this
 // device actually sustains for each traffic mix, the practical ceiling next to
-// the 8 TB/s data-sheet peak.
+// the 8 TB/s data-sheet peak.  A fourth probe measures the fp32 FMA rate the
+// vector ALUs sustain without packed instructions (the kernels are built
+// without them), the arithmetic ceiling next to the derived VALU peak.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -51,7 +53,36 @@ __global__ void __launch_bounds__(kProbeThreads) k_stream_copy(const f4* __restr
     for (; i < n4; i += bd) __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
 }
 
+// Eight independent FMA chains per lane (enough to cover the FMA latency),
+// non-packed fp32; the result is consumed by a store that no finite value
+// takes.  Every workgroup runs the same work: kValuBlocks x 256 threads x
+// iters x 8 FMAs.
+constexpr int kValuBlocks = 2048;    // 8 waves per SIMD on 256 CUs
+constexpr int kValuChains = 8;
+
+__global__ void __launch_bounds__(kProbeThreads) k_valu_fma(float* __restrict__ sink, long iters, float a) {
+    float acc[kValuChains];
+#pragma unroll
+    for (int k = 0; k < kValuChains; ++k) acc[k] = 1e-3f * threadIdx.x + k;
+    for (long i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int k = 0; k < kValuChains; ++k) acc[k] = __builtin_fmaf(acc[k], a, 0.5f);
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kValuChains; ++k) t += acc[k];
+    if (t != t && threadIdx.x == 0) sink[0] = t;
+}
+
 }  // namespace
+
+hipError_t launch_valu_probe(long iters, float* dst, hipStream_t st) {
+    if (iters == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_valu_fma, dim3(kValuBlocks), dim3(kProbeThreads), 0, st, dst, iters, 0.999f);
+    return hipGetLastError();
+}
+
+long valu_probe_fmas(long iters) { return (long)kValuBlocks * kProbeThreads * kValuChains * iters; }
 
 hipError_t launch_stream_probe(int kind, const float* src, float* dst, long n_floats, hipStream_t st) {
     const long n4 = n_floats / 4;

@@ -19,6 +19,7 @@ Shapes (channel index fastest, D_l = (l+1)^2, P and D_out from `layout`):
 from __future__ import annotations
 
 import ctypes
+import functools
 
 import numpy as np
 import torch
@@ -37,6 +38,7 @@ def _p(t):
 
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
 
 
 def _want(t, name, shape, dtype=torch.float32, device=None):
@@ -88,13 +90,20 @@ def paths(l_in: int, l_sh: int = None, l_out: int = None):
 def layout(lmax, variant: int = SUMMED):
     """(paths, out_dim) of a variant: the path list in w's order and the
     number of output components per channel."""
-    a, b, c = degrees(lmax)
+    ps, d = _layout(degrees(lmax), int(variant))
+    return list(ps), d
+
+
+@functools.lru_cache(maxsize=None)
+def _layout(deg, variant):
+    # the library's answer for a (degrees, variant) pair never changes: asked once
+    a, b, c = deg
     n, d = ctypes.c_int32(0), ctypes.c_int32(0)
     check(lib().conv_tp_layout(variant, a, b, c, ctypes.byref(n), ctypes.byref(d), None))
     buf = np.zeros((n.value, 3), dtype=np.int32)
     check(lib().conv_tp_layout(variant, a, b, c, ctypes.byref(n), ctypes.byref(d),
                                buf.ctypes.data_as(ctypes.c_void_p)))
-    return [tuple(int(v) for v in r) for r in buf], int(d.value)
+    return tuple(tuple(int(v) for v in r) for r in buf), int(d.value)
 
 
 def coupling(l1: int, l2: int, l3: int) -> np.ndarray:
@@ -165,12 +174,12 @@ def _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant=SUMMED):
     c = x.shape[2]
     _want(x, "x", (n, dim(l_in), c), device=graph.device)
     _want(y_or_vec, "y_or_vec", (e, dim(l_sh) if y_mode == Y_GIVEN else 3), device=graph.device)
-    _want(w, "w", (e, len(layout(lmax, variant)[0]), c), device=graph.device)
+    _want(w, "w", (e, len(_layout(degrees(lmax), int(variant))[0]), c), device=graph.device)
     return n, e, c
 
 
 def out_dim(lmax, variant: int = SUMMED) -> int:
-    return layout(lmax, variant)[1]
+    return _layout(degrees(lmax), int(variant))[1]
 
 
 def conv_tp_fwd(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN, algo: int = ALGO_CSR,
@@ -188,8 +197,9 @@ def conv_tp_fwd(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN, 
 
 
 def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN,
-                dx=None, dw=None, dy=None, variant: int = SUMMED):
-    """(dx, dw, dY or dvec) for upstream gradient grad_out (see include/convtp.h)."""
+                dx=None, dw=None, dy=None, variant: int = SUMMED, algo: int = ALGO_CSR):
+    """(dx, dw, dY or dvec) for upstream gradient grad_out (see include/convtp.h);
+    algo ALGO_FRAME computes it in each edge's frame (edge vectors)."""
     n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant)
     _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
     send_ptr, send_perm, send_recv = graph.transpose
@@ -199,7 +209,7 @@ def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int =
     _want(dx, "dx", x.shape, device=x.device)
     _want(dw, "dw", w.shape, device=x.device)
     _want(dy, "dy", y_or_vec.shape, device=x.device)
-    prob = _problem(n, e, c, lmax, y_mode, ALGO_CSR, variant)
+    prob = _problem(n, e, c, lmax, y_mode, algo, variant)
     check(lib().conv_tp_bwd(ctypes.byref(prob), _p(grad_out), _p(x), _p(y_or_vec), _p(w),
                             _p(graph.row_ptr), _p(graph.senders), _p(send_ptr), _p(send_perm),
                             _p(send_recv), _p(dx), _p(dw), _p(dy), _stream(x)))
@@ -213,7 +223,7 @@ def conv_tp_bwd_dy(grad_out, x, w, graph: Graph, lmax: int, dy=None, variant: in
     if graph.n_nodes != n or graph.senders.numel() != e:
         raise ValueError("graph does not match x / w")
     _want(x, "x", (n, dim(l_in), c))
-    _want(w, "w", (e, len(layout(lmax, variant)[0]), c), device=x.device)
+    _want(w, "w", (e, len(_layout(degrees(lmax), int(variant))[0]), c), device=x.device)
     _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
     dy = torch.empty((e, dim(l_sh)), dtype=torch.float32, device=x.device) if dy is None else dy
     _want(dy, "dy", (e, dim(l_sh)), device=x.device)
@@ -364,6 +374,15 @@ def stream_probe(kind: int, src, dst):
         if a is not None:
             _want(a, name, (a.numel(),), device=t.device)
     check(lib().conv_tp_stream_probe(kind, _p(src), _p(dst), n, _stream(t)))
+
+
+def valu_probe(iterations: int, sink):
+    """fp32 FMA probe (measurement only): launches it on sink's device and
+    returns the number of FMAs the launch performs."""
+    _want(sink, "sink", (sink.numel(),))
+    fmas = ctypes.c_int64(0)
+    check(lib().conv_tp_valu_probe(int(iterations), _p(sink), ctypes.byref(fmas), _stream(sink)))
+    return int(fmas.value)
 
 
 def spherical_harmonics_jvp(vec, a_vec, lmax: int, out=None):

@@ -47,6 +47,8 @@ hipError_t launch_node_bwd(int, int, int, const float*, const float*, const floa
 hipError_t launch_stream_probe(int, const float*, float*, long n, hipStream_t) {
     return n == 0 ? hipSuccess : hipErrorNotSupported;
 }
+hipError_t launch_valu_probe(long n, float*, hipStream_t) { return n == 0 ? hipSuccess : hipErrorNotSupported; }
+long valu_probe_fmas(long n) { return n; }
 hipError_t launch_check_graph(int, int, const int32_t*, const int32_t*, unsigned long long*, hipStream_t) {
     return hipErrorNotSupported;
 }

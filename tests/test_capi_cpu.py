@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 106
+    assert L.conv_tp_version() == 107
 
 
 def test_paths_match_oracle(capi):
@@ -123,7 +123,14 @@ def test_frame_forward_rejections(capi):
     assert "edge frame" in capi.lib().conv_tp_last_error().decode()
     assert _fwd(capi, _prob(capi, algo=3, y_mode=1)) == capi.CTP_EINVAL
     assert _fwd(capi, _prob(capi, algo=2, y_mode=1), x=NUL) == capi.CTP_EINVAL
-    assert _bwd(capi, _prob(capi, algo=2, y_mode=1)) == capi.CTP_EUNSUPPORTED
+    # the edge-frame backward (algo 2) likewise; the message backwards have no frame form
+    assert _bwd(capi, _prob(capi, algo=2, y_mode=0)) == capi.CTP_EUNSUPPORTED
+    assert _bwd(capi, _prob(capi, algo=2, y_mode=1, variant=1)) == capi.CTP_EUNSUPPORTED
+    assert _bwd(capi, _empty(capi, algo=2, y_mode=1), g=NUL, x=NUL, y=NUL, w=NUL, s=NUL, pe=NUL, sr=NUL,
+                dx=NUL, dw=NUL, dy=NUL) == capi.CTP_OK
+    assert _bwd_msg(capi, _prob(capi, algo=2, y_mode=1)) == capi.CTP_EUNSUPPORTED
+    assert capi.lib().conv_tp_bwd_msg_noalloc(ctypes.byref(_prob(capi, algo=2, y_mode=1)), *([A] * 9),
+                                              A2, A2, A2, NUL) == capi.CTP_EUNSUPPORTED
 
 
 def _empty(capi, **kw):
@@ -310,6 +317,11 @@ def test_other_entry_points_validate(capi):
     assert L.conv_tp_stream_probe(1, NUL, NUL, 16, NUL) == capi.CTP_EINVAL
     assert L.conv_tp_stream_probe(0, MIS, A2, 16, NUL) == capi.CTP_EALIGN
     assert L.conv_tp_stream_probe(2, A, A2, 0, NUL) == capi.CTP_OK
+    fm = ctypes.c_int64(-1)
+    assert L.conv_tp_valu_probe(-1, A, ctypes.byref(fm), NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_valu_probe(5, A, None, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_valu_probe(5, NUL, ctypes.byref(fm), NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_valu_probe(0, A, ctypes.byref(fm), NUL) == capi.CTP_OK and fm.value == 0
 
 
 def test_header_is_plain_c99(tmp_path):

@@ -188,3 +188,61 @@ def test_double_bwd_1024_channels(ctp, dev, variant):
     again = ctp.conv_tp_bwd_bwd(*args, g, deg, variant=variant)
     for u, v in zip(res, again):
         assert torch.equal(u, v)
+
+
+# ------------------------------------------------------------ backward in each edge's frame (algo 2)
+
+
+def check_frame_bwd(ctp, dev, deg, n, c, seed, vec_edit=None, mean_deg=10.0):
+    prob, d = workload(deg, n, c, 0, seed, mean_deg=mean_deg)
+    vec = d["vec"].copy()
+    if vec_edit is not None:
+        vec_edit(vec)
+    l_sh = deg[1]
+    v64 = vec.astype(np.float64)
+    Y = osh.real_sh(l_sh, v64)
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w, G, vt = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev), T(vec, dev)
+    print(f"[frame bwd] deg={deg} n={n} c={c}", flush=True)
+    dx, dw, dvec = ctp.conv_tp_bwd(G, x, vt, w, g, deg, ctp.VEC_GIVEN, algo=ctp.ALGO_FRAME)
+    sp, pe, sr = og.transpose(n, d["row_ptr"], d["senders"])
+    close("dx", host(dx), oc.bwd_dx(prob, Y, d["w"], d["grad_out"], sp, pe, sr))
+    ref_dw, ref_dY = oc.bwd_edges(prob, d["x"], Y, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+    close("dw", host(dw), ref_dw)
+    close("dvec", host(dvec), osh.vec_grad_from_sh_grad(l_sh, v64, ref_dY),
+          nonzero=any(p[1] > 0 for p in prob.paths))
+    again = ctp.conv_tp_bwd(G, x, vt, w, g, deg, ctp.VEC_GIVEN, algo=ctp.ALGO_FRAME)
+    for u, v in zip((dx, dw, dvec), again):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("deg", TRIPLES + [(3, 3, 3), (1, 1, 1)])
+def test_frame_backward_small(ctp, dev, deg):
+    check_frame_bwd(ctp, dev, deg, 70, 96, seed=sum(deg) + 40)
+
+
+def test_frame_backward_poles_and_zero_vectors(ctp, dev):
+    def edit(v):
+        v[::17] = 0.0                        # zero vectors: only the l2 = 0 paths, dvec = 0
+        v[1::19] = (0.0, 0.0, 1.0)           # north pole
+        v[2::23] = (0.0, 0.0, -1.0)          # south pole
+        v[3::29] = (1e-4, -2e-4, -0.7)       # near the south pole
+        v[4::31] *= 7.5                      # lengths other than one
+    check_frame_bwd(ctp, dev, (3, 3, 3), 60, 64, seed=77, vec_edit=edit)
+    check_frame_bwd(ctp, dev, (2, 3, 1), 60, 64, seed=78, vec_edit=edit)
+
+
+@pytest.mark.parametrize("c", [1024, 640, 128])
+def test_frame_backward_channel_tiles_and_unsplit_grid(ctp, dev, c):
+    # N = 4096 at C >= 128 is above the small-grid split threshold
+    n = 4096 if c == 128 else 30
+    check_frame_bwd(ctp, dev, (3, 3, 3), n, c, seed=c, mean_deg=3.0 if n > 100 else 10.0)
+
+
+def test_frame_backward_rejections(ctp, dev):
+    prob, d = workload((2, 2, 2), 10, 16, 0, seed=1)
+    g = ctp.Graph(10, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w, G = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev)
+    Y = T(osh.real_sh(2, d["vec"].astype(np.float64)).astype(np.float32), dev)
+    with pytest.raises(ctp.ConvTPError):
+        ctp.conv_tp_bwd(G, x, Y, w, g, 2, ctp.Y_GIVEN, algo=ctp.ALGO_FRAME)
