@@ -258,6 +258,28 @@ int32_t conv_tp_sh_jvp(int32_t n_edges, int32_t l_sh, const float *vec, const fl
 int32_t conv_tp_sh_bwd_bwd(int32_t n_edges, int32_t l_sh, const float *vec, const float *dY, const float *a_vec,
                            const float *g_y, float *g_vec, void *stream);
 
+/* The same VJP of the edge-vector backward in one call (FlashCart, section
+ * on symbolic VJPs: the second-order pass of force training), the steps
+ * above on `stream` in order: Y = conv_tp_sh(vec), a_y = conv_tp_sh_jvp(vec,
+ * a_vec), dY = conv_tp_bwd_dy (only if dY is NULL), (g_x, g_w, g_y, g_grad) =
+ * conv_tp_bwd_bwd, g_vec = conv_tp_sh_bwd_bwd(vec, dY, a_vec, g_y).
+ * dY [E][D_sh] is the first backward's harmonic gradient (conv_tp_bwd with Y
+ * = conv_tp_sh(vec) given) when the caller kept it, which saves its
+ * recomputation; NULL computes it.  prob: y_mode 1, algo 0, either variant.
+ * Inputs and outputs as for conv_tp_bwd_bwd with vec[E][3], a_vec[E][3] and
+ * g_vec[E][3] in place of Y, a_y, g_y.  workspace: device, 16-byte aligned,
+ * at least conv_tp_bwd_bwd_vec_workspace bytes (Y, a_y and g_y, plus dY when
+ * not given, [E][D_sh] fp32 each), caller-owned, contents undefined after
+ * the call; CTP_EINVAL if smaller.  Bitwise reproducible as
+ * conv_tp_bwd_bwd. */
+int32_t conv_tp_bwd_bwd_vec(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *vec,
+                            const float *w, const float *a_x, const float *a_w, const float *a_vec, const float *dY,
+                            const int32_t *row_ptr, const int32_t *senders, const int32_t *send_ptr,
+                            const int32_t *send_perm, const int32_t *send_recv, float *g_x, float *g_w, float *g_vec,
+                            float *g_grad, float *workspace, int64_t workspace_bytes, void *stream);
+/* Workspace bytes conv_tp_bwd_bwd_vec needs; dy_given: whether dY is passed. */
+int32_t conv_tp_bwd_bwd_vec_workspace(const conv_tp_problem *prob, int32_t dy_given, int64_t *bytes);
+
 /* Sender-sorted transpose of a CSR-by-receiver graph (the ordering of edges
  * by sender that FlashCart's section 4 names for deterministic gradients of
  * shared inputs): send_ptr[N+1], send_perm[E] (CSR edge ids, ascending within
@@ -332,7 +354,7 @@ const char *conv_tp_last_error(void);
  * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward), 104 conv_tp_bwd_dy, 105
  * independent degrees, up to 1024 channels in every backward and variant 1
  * in conv_tp_bwd_bwd, 106 conv_tp_bwd_msg_noalloc, 107 conv_tp_valu_probe and algo 2 in
- * conv_tp_bwd. */
+ * conv_tp_bwd, 108 conv_tp_bwd_bwd_vec. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

@@ -20,6 +20,7 @@ STATUS_NAMES = {0: "CTP_OK", 1: "CTP_EINVAL", 2: "CTP_EUNSUPPORTED", 3: "CTP_EAL
 # Every symbol include/convtp.h declares.
 EXPORTS = ("conv_tp_num_paths", "conv_tp_paths", "conv_tp_layout", "conv_tp_coupling", "conv_tp_fwd", "conv_tp_bwd",
            "conv_tp_bwd_msg_workspace", "conv_tp_bwd_msg", "conv_tp_bwd_msg_noalloc", "conv_tp_bwd_dy", "conv_tp_bwd_bwd",
+           "conv_tp_bwd_bwd_vec", "conv_tp_bwd_bwd_vec_workspace",
            "conv_tp_sh", "conv_tp_sh_bwd", "conv_tp_build_transpose", "conv_tp_check_graph",
            "conv_tp_sh_jvp", "conv_tp_sh_bwd_bwd", "conv_tp_node_fwd", "conv_tp_node_bwd", "conv_tp_stream_probe", "conv_tp_valu_probe", "conv_tp_last_error",
            "conv_tp_version")
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "conv_tp_bwd_msg": ([pp] + [vp] * 13 + [ctypes.c_int64, vp], i32),
         "conv_tp_bwd_msg_noalloc": ([pp] + [vp] * 13, i32),
         "conv_tp_bwd_bwd": ([pp] + [vp] * 17, i32),
+        "conv_tp_bwd_bwd_vec": ([pp] + [vp] * 18 + [ctypes.c_int64, vp], i32),
+        "conv_tp_bwd_bwd_vec_workspace": ([pp, i32, i64p], i32),
         "conv_tp_sh": ([i32, i32, vp, vp, vp], i32),
         "conv_tp_sh_bwd": ([i32, i32, vp, vp, vp, vp], i32),
         "conv_tp_sh_jvp": ([i32, i32, vp, vp, vp, vp], i32),

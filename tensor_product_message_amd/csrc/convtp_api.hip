@@ -210,7 +210,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 107; }
+int32_t conv_tp_version(void) { return 108; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
@@ -410,6 +410,107 @@ int32_t conv_tp_bwd_bwd(const conv_tp_problem* prob, const float* grad_out, cons
     a.g_y = g_y;
     a.g_grad = g_grad;
     return hip_status(ctp::launch_double_bwd(a, static_cast<hipStream_t>(stream)), "conv_tp_bwd_bwd launch");
+}
+
+// Y, a_y and g_y, plus dY when the caller does not pass it: [E][D_sh] fp32 each.
+int64_t dd_vec_workspace_bytes(const Shape& s, bool dy_given) {
+    return (dy_given ? 3 : 4) * s.E * s.D2 * (int64_t)sizeof(float);
+}
+
+int32_t conv_tp_bwd_bwd_vec_workspace(const conv_tp_problem* prob, int32_t dy_given, int64_t* bytes) {
+    Shape s{};
+    if (int r = check_problem(prob, &s)) return r;
+    if (bytes == nullptr) return fail(CTP_EINVAL, "bytes is null");
+    *bytes = dd_vec_workspace_bytes(s, dy_given != 0);
+    return ok();
+}
+
+int32_t conv_tp_bwd_bwd_vec(const conv_tp_problem* prob, const float* grad_out, const float* x, const float* vec,
+                            const float* w, const float* a_x, const float* a_w, const float* a_vec, const float* dY,
+                            const int32_t* row_ptr, const int32_t* senders, const int32_t* send_ptr,
+                            const int32_t* send_perm, const int32_t* send_recv, float* g_x, float* g_w,
+                            float* g_vec, float* g_grad, float* workspace, int64_t workspace_bytes, void* stream) {
+    Shape s{};
+    if (int r = check_problem(prob, &s)) return r;
+    if (prob->algo != 0) return fail(CTP_EUNSUPPORTED, "the double backward has only the deterministic algorithm");
+    if (prob->y_mode != 1) return fail(CTP_EUNSUPPORTED, "conv_tp_bwd_bwd_vec takes edge vectors (y_mode 1)");
+    if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
+    if (int r = need(x, s.N * s.D1 * s.C, 16, "x")) return r;
+    if (int r = need(vec, s.E * 3, 4, "vec")) return r;
+    if (int r = need(w, s.E * s.P * s.C, 16, "w")) return r;
+    if (int r = need(a_x, s.N * s.D1 * s.C, 16, "a_x")) return r;
+    if (int r = need(a_w, s.E * s.P * s.C, 16, "a_w")) return r;
+    if (int r = need(a_vec, s.E * 3, 4, "a_vec")) return r;
+    if (int r = need(dY, 0, 4, "dY")) return r;   // optional
+    if (int r = need(row_ptr, s.N + 1, 4, "row_ptr")) return r;
+    if (int r = need(senders, s.E, 4, "senders")) return r;
+    if (int r = need(send_ptr, s.N + 1, 4, "send_ptr")) return r;
+    if (int r = need(send_perm, s.E, 4, "send_perm")) return r;
+    if (int r = need(send_recv, s.E, 4, "send_recv")) return r;
+    if (int r = need(g_x, s.N * s.D1 * s.C, 16, "g_x")) return r;
+    if (int r = need(g_w, s.E * s.P * s.C, 16, "g_w")) return r;
+    if (int r = need(g_vec, s.E * 3, 4, "g_vec")) return r;
+    if (int r = need(g_grad, s.N * s.D3 * s.C, 16, "g_grad")) return r;
+    const int64_t need_bytes = dd_vec_workspace_bytes(s, dY != nullptr);
+    if (workspace_bytes < need_bytes)
+        return fail(CTP_EINVAL, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)need_bytes);
+    if (int r = need(workspace, need_bytes / (int64_t)sizeof(float), 16, "workspace")) return r;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t ed = s.E * s.D2;
+    float* Y = workspace;
+    float* a_y = workspace + ed;
+    float* g_y = workspace + 2 * ed;
+    const float* dYv = dY;
+    if (s.E > 0) {
+        if (hipError_t e = ctp::launch_sh(prob->l_sh, s.E, vec, Y, st); e != hipSuccess)
+            return hip_status(e, "conv_tp_bwd_bwd_vec: harmonics");
+        if (hipError_t e = ctp::launch_sh_jvp(prob->l_sh, s.E, vec, a_vec, a_y, st); e != hipSuccess)
+            return hip_status(e, "conv_tp_bwd_bwd_vec: harmonic JVP");
+    }
+    if (dYv == nullptr) {
+        float* dYw = workspace + 3 * ed;
+        ctp::LaunchArgs a = base_args(prob);
+        a.vec_mode = 0;
+        a.grad = grad_out;
+        a.x = x;
+        a.w = w;
+        a.row_ptr = row_ptr;
+        a.senders = senders;
+        a.dy = dYw;
+        if (hipError_t e = ctp::launch_bwd_dy(a, st); e != hipSuccess)
+            return hip_status(e, "conv_tp_bwd_bwd_vec: harmonic gradient");
+        dYv = dYw;
+    }
+    ctp::DoubleArgs a{};
+    a.l_in = prob->l_in;
+    a.l_sh = prob->l_sh;
+    a.l_out = prob->l_out;
+    a.variant = prob->variant;
+    a.n_nodes = prob->n_nodes;
+    a.n_edges = prob->n_edges;
+    a.C = prob->channels;
+    a.x = x;
+    a.ax = a_x;
+    a.y = Y;
+    a.ay = a_y;
+    a.w = w;
+    a.aw = a_w;
+    a.grad = grad_out;
+    a.row_ptr = row_ptr;
+    a.senders = senders;
+    a.send_ptr = send_ptr;
+    a.send_perm = send_perm;
+    a.send_recv = send_recv;
+    a.g_x = g_x;
+    a.g_w = g_w;
+    a.g_y = g_y;
+    a.g_grad = g_grad;
+    if (hipError_t e = ctp::launch_double_bwd(a, st); e != hipSuccess)
+        return hip_status(e, "conv_tp_bwd_bwd_vec: double backward");
+    if (s.E == 0) return ok();
+    return hip_status(ctp::launch_sh_bwd_bwd(prob->l_sh, s.E, vec, dYv, a_vec, g_y, g_vec, st),
+                      "conv_tp_bwd_bwd_vec: harmonic second-order term");
 }
 
 int32_t conv_tp_sh(int32_t n_edges, int32_t l_sh, const float* vec, float* Y, void* stream) {

@@ -408,17 +408,38 @@ def spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, lmax: int, out=None):
     return out
 
 
-def conv_tp_bwd_bwd_vec(grad_out, x, vec, w, a_x, a_w, a_vec, graph: Graph, lmax, variant: int = SUMMED):
-    """VJP of the edge-vector backward: (g_x, g_w, g_vec, g_grad) for
-    cotangents (a_x, a_w, a_vec) of (dx, dw, dvec), by the library calls
-    include/convtp.h lists (harmonics, the first backward's dY alone, harmonic
-    JVP, the double backward, and the harmonic second-order term)."""
-    l_sh = degrees(lmax)[1]
-    Y = spherical_harmonics(vec, l_sh)
-    dY = conv_tp_bwd_dy(grad_out, x, w, graph, lmax, variant=variant)
-    a_y = spherical_harmonics_jvp(vec, a_vec, l_sh)
-    g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd(grad_out, x, Y, w, a_x, a_w, a_y, graph, lmax, variant=variant)
-    g_vec = spherical_harmonics_bwd_bwd(vec, dY, a_vec, g_y, l_sh)
+def conv_tp_bwd_bwd_vec(grad_out, x, vec, w, a_x, a_w, a_vec, graph: Graph, lmax, variant: int = SUMMED,
+                        dY=None, out=None, workspace=None):
+    """VJP of the edge-vector backward in one library call
+    (conv_tp_bwd_bwd_vec, include/convtp.h): (g_x, g_w, g_vec, g_grad) for
+    cotangents (a_x, a_w, a_vec) of (dx, dw, dvec).  dY: the first backward's
+    harmonic gradient [E][(l_sh+1)^2] if the caller kept it (else the library
+    recomputes it).  workspace: a float32 device tensor of at least
+    conv_tp_bwd_bwd_vec_workspace bytes, allocated here if None."""
+    n, e, c = _shapes(x, vec, w, graph, lmax, VEC_GIVEN, variant)
+    _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
+    _want(a_x, "a_x", x.shape, device=x.device)
+    _want(a_w, "a_w", w.shape, device=x.device)
+    _want(a_vec, "a_vec", vec.shape, device=x.device)
+    if dY is not None:
+        _want(dY, "dY", (e, dim(degrees(lmax)[1])), device=x.device)
+    send_ptr, send_perm, send_recv = graph.transpose
+    if out is None:
+        out = (torch.empty_like(x), torch.empty_like(w), torch.empty_like(vec), torch.empty_like(grad_out))
+    g_x, g_w, g_vec, g_grad = out
+    for name, t, ref in (("g_x", g_x, x), ("g_w", g_w, w), ("g_vec", g_vec, vec), ("g_grad", g_grad, grad_out)):
+        _want(t, name, ref.shape, device=x.device)
+    prob = _problem(n, e, c, lmax, VEC_GIVEN, ALGO_CSR, variant)
+    if workspace is None:
+        nbytes = ctypes.c_int64()
+        check(lib().conv_tp_bwd_bwd_vec_workspace(ctypes.byref(prob), int(dY is not None), ctypes.byref(nbytes)))
+        workspace = torch.empty(max(1, nbytes.value // 4), dtype=torch.float32, device=x.device)
+    if workspace.dtype != torch.float32 or workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 tensor on x's device")
+    check(lib().conv_tp_bwd_bwd_vec(ctypes.byref(prob), _p(grad_out), _p(x), _p(vec), _p(w), _p(a_x), _p(a_w),
+                                    _p(a_vec), _p(dY), _p(graph.row_ptr), _p(graph.senders), _p(send_ptr),
+                                    _p(send_perm), _p(send_recv), _p(g_x), _p(g_w), _p(g_vec), _p(g_grad),
+                                    _p(workspace), workspace.numel() * 4, _stream(x)))
     return g_x, g_w, g_vec, g_grad
 
 
@@ -437,8 +458,10 @@ class ConvTPFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_out):
         x, y_or_vec, w = ctx.saved_tensors
+        # grad mode is on here only under create_graph: then the second
+        # backward follows, and the edge-vector path keeps its harmonic gradient
         dx, dy, dw = ConvTPBackward.apply(grad_out.contiguous(), x, y_or_vec, w, ctx.graph, ctx.lmax,
-                                          ctx.y_mode, ctx.variant)
+                                          ctx.y_mode, ctx.variant, torch.is_grad_enabled())
         return dx, dy, dw, None, None, None, None
 
 
@@ -446,29 +469,37 @@ class ConvTPBackward(torch.autograd.Function):
     """The VJP as a function of (grad_out, x, Y or vec, w), returning
     (dx, dY or dvec, dw): conv_tp_bwd (variant 0) or conv_tp_bwd_msg with a
     workspace from torch's allocator (variant 1, whose grad_out rows are much
-    wider than x's).  Its own VJP (the VJP of the VJP) is conv_tp_bwd_bwd, with
-    the harmonics' second-order terms for edge vectors (conv_tp_bwd_bwd_vec)."""
+    wider than x's).  With edge vectors and keep_dy it runs on Y = harmonics of
+    vec and keeps dY, the harmonic gradient, for its own VJP (the VJP of the
+    VJP): conv_tp_bwd_bwd, or conv_tp_bwd_bwd_vec for edge vectors."""
 
     @staticmethod
-    def forward(ctx, grad_out, x, y_or_vec, w, graph, lmax, y_mode, variant):
-        ctx.save_for_backward(grad_out, x, y_or_vec, w)
-        ctx.graph, ctx.lmax, ctx.y_mode, ctx.variant = graph, lmax, y_mode, variant
+    def forward(ctx, grad_out, x, y_or_vec, w, graph, lmax, y_mode, variant, keep_dy=False):
         bwd = conv_tp_bwd_msg if variant == SLOTS else conv_tp_bwd
-        dx, dw, dy = bwd(grad_out, x, y_or_vec, w, graph, lmax, y_mode, variant=variant)
+        dY = None
+        if y_mode == VEC_GIVEN and keep_dy:
+            l_sh = degrees(lmax)[1]
+            Y = spherical_harmonics(y_or_vec, l_sh)
+            dx, dw, dY = bwd(grad_out, x, Y, w, graph, lmax, Y_GIVEN, variant=variant)
+            dy = spherical_harmonics_backward(y_or_vec, dY, l_sh)
+        else:
+            dx, dw, dy = bwd(grad_out, x, y_or_vec, w, graph, lmax, y_mode, variant=variant)
+        ctx.save_for_backward(grad_out, x, y_or_vec, w, dY)
+        ctx.graph, ctx.lmax, ctx.y_mode, ctx.variant = graph, lmax, y_mode, variant
         return dx, dy, dw
 
     @staticmethod
     @torch.autograd.function.once_differentiable
     def backward(ctx, a_x, a_y, a_w):
-        G, x, y_or_vec, w = ctx.saved_tensors
+        G, x, y_or_vec, w, dY = ctx.saved_tensors
         a_x, a_y, a_w = a_x.contiguous(), a_y.contiguous(), a_w.contiguous()
         if ctx.y_mode == Y_GIVEN:
             g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd(G, x, y_or_vec, w, a_x, a_w, a_y, ctx.graph, ctx.lmax,
                                                     variant=ctx.variant)
         else:
             g_x, g_w, g_y, g_grad = conv_tp_bwd_bwd_vec(G, x, y_or_vec, w, a_x, a_w, a_y, ctx.graph, ctx.lmax,
-                                                        variant=ctx.variant)
-        return g_grad, g_x, g_y, g_w, None, None, None, None
+                                                        variant=ctx.variant, dY=dY)
+        return g_grad, g_x, g_y, g_w, None, None, None, None, None
 
 
 def conv_tp(x, y_or_vec, w, graph: Graph, lmax, y_mode: int = Y_GIVEN, variant: int = SUMMED):

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 107
+    assert L.conv_tp_version() == 108
 
 
 def test_paths_match_oracle(capi):
@@ -273,6 +273,44 @@ def test_bwd_bwd_rejections(capi):
     a = [NUL] * 16
     a[7] = a[9] = A     # empty graph: only row_ptr and send_ptr (N+1 = 1 entry); nothing is launched
     assert _bwd_bwd(capi, _prob(capi, n_nodes=0, n_edges=0), a) == capi.CTP_OK
+
+
+def _bwd_bwd_vec(capi, prob, args, ws_bytes):
+    return capi.lib().conv_tp_bwd_bwd_vec(ctypes.byref(prob), *args, ws_bytes, NUL)
+
+
+def test_bwd_bwd_vec_rejections_and_workspace(capi):
+    L = capi.lib()
+    nb = ctypes.c_int64(-1)
+    p = _prob(capi, y_mode=1, l_sh=2)   # E = 8, D_sh = 9
+    assert L.conv_tp_bwd_bwd_vec_workspace(ctypes.byref(p), 1, ctypes.byref(nb)) == capi.CTP_OK
+    assert nb.value == 3 * 8 * 9 * 4
+    assert L.conv_tp_bwd_bwd_vec_workspace(ctypes.byref(p), 0, ctypes.byref(nb)) == capi.CTP_OK
+    assert nb.value == 4 * 8 * 9 * 4
+    assert L.conv_tp_bwd_bwd_vec_workspace(ctypes.byref(p), 0, None) == capi.CTP_EINVAL
+    # grad_out x vec w a_x a_w a_vec dY row_ptr senders send_ptr send_perm send_recv | 4 outputs | workspace
+    args = [A] * 13 + [A2] * 4 + [A]
+    big = 1 << 20
+    assert len(args) + 3 == len(L.conv_tp_bwd_bwd_vec.argtypes)
+    assert _bwd_bwd_vec(capi, _prob(capi, y_mode=0), args, big) == capi.CTP_EUNSUPPORTED
+    assert _bwd_bwd_vec(capi, _prob(capi, y_mode=1, algo=2), args, big) == capi.CTP_EUNSUPPORTED
+    assert _bwd_bwd_vec(capi, _prob(capi, y_mode=1, channels=1025), args, big) == capi.CTP_EUNSUPPORTED
+    for k in range(18):
+        if k == 7:
+            continue    # dY is optional
+        a = list(args)
+        a[k] = NUL
+        assert _bwd_bwd_vec(capi, p, a, big) == capi.CTP_EINVAL, k
+    assert _bwd_bwd_vec(capi, p, args, 3 * 8 * 9 * 4 - 4) == capi.CTP_EINVAL       # dY given: 3 arrays
+    a = list(args)
+    a[7] = NUL
+    assert _bwd_bwd_vec(capi, p, a, 3 * 8 * 9 * 4) == capi.CTP_EINVAL              # dY computed: 4 arrays
+    a = list(args)
+    a[17] = MIS
+    assert _bwd_bwd_vec(capi, p, a, big) == capi.CTP_EALIGN
+    a = [NUL] * 18
+    a[8] = a[10] = A    # empty graph: only row_ptr and send_ptr; nothing is launched
+    assert _bwd_bwd_vec(capi, _prob(capi, y_mode=1, n_nodes=0, n_edges=0), a, 0) == capi.CTP_OK
 
 
 def test_empty_arrays_may_be_null(capi):

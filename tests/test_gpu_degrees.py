@@ -246,3 +246,57 @@ def test_frame_backward_rejections(ctp, dev):
     Y = T(osh.real_sh(2, d["vec"].astype(np.float64)).astype(np.float32), dev)
     with pytest.raises(ctp.ConvTPError):
         ctp.conv_tp_bwd(G, x, Y, w, g, 2, ctp.Y_GIVEN, algo=ctp.ALGO_FRAME)
+
+
+# ------------------------------------------------------------ small grids: edge lists split between workgroups
+
+
+def skewed_graph(n, c, l_in, l_sh, n_paths, out_dim, seed):
+    """In-degrees 0, 1, 2, ... 13, 25 and a hub of 300, and the same out-degrees
+    in another node order (edges paired at random), so that both the receiver
+    lists (the forward) and the sender lists (the backward) run shorter than,
+    equal to and longer than every chunk count; a few zero and polar edge
+    vectors."""
+    rng = np.random.default_rng(seed)
+    indeg = np.array([(0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 13, 25)[k % 13] for k in range(n)])
+    indeg[n // 2] = 300
+    recv = np.repeat(np.arange(n), indeg)
+    e = recv.size
+    send = rng.permutation(np.repeat(rng.permutation(n), indeg)).astype(np.int32)
+    vec = rng.standard_normal((e, 3)).astype(np.float32)
+    vec[::29] = 0.0
+    vec[1::31] = (0.0, 0.0, 1.5)
+    vec[2::37] = (0.0, 0.0, -0.5)
+    d1, d2 = (l_in + 1) ** 2, (l_sh + 1) ** 2
+    return dict(n_nodes=n, n_edges=e, row_ptr=og.row_ptr_from_receivers(recv, n), senders=send, vec=vec,
+                x=rng.standard_normal((n, d1, c)).astype(np.float32),
+                w=rng.standard_normal((e, n_paths, c)).astype(np.float32),
+                grad_out=rng.standard_normal((n, out_dim, c)).astype(np.float32))
+
+
+@pytest.mark.parametrize("c", [16, 64, 100, 128, 192, 256, 320])
+def test_frame_small_grid_split(ctp, dev, c):
+    """Edge-frame forward and backward on grids small enough to split every
+    edge list between two workgroups (lists of 0, 1, 2, ... edges and a hub),
+    at one to five waves of channels: element by element against the oracle,
+    bitwise equal reruns."""
+    deg = (3, 3, 3) if c <= 128 else (2, 3, 1)
+    prob = oc.Problem(*deg)
+    n = 40
+    d = skewed_graph(n, c, deg[0], deg[1], prob.P, prob.D3, seed=c)
+    v64 = d["vec"].astype(np.float64)
+    Y = osh.real_sh(deg[1], v64)
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w, G, vt = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev), T(d["vec"], dev)
+    print(f"[frame split] deg={deg} n={n} e={d['n_edges']} c={c}", flush=True)
+    out = ctp.conv_tp_fwd(x, vt, w, g, deg, ctp.VEC_GIVEN, ctp.ALGO_FRAME)
+    close("out", host(out), oc.fwd(prob, d["x"], Y, d["w"], d["row_ptr"], d["senders"]))
+    assert torch.equal(out, ctp.conv_tp_fwd(x, vt, w, g, deg, ctp.VEC_GIVEN, ctp.ALGO_FRAME))
+    dx, dw, dvec = ctp.conv_tp_bwd(G, x, vt, w, g, deg, ctp.VEC_GIVEN, algo=ctp.ALGO_FRAME)
+    sp, pe, sr = og.transpose(n, d["row_ptr"], d["senders"])
+    close("dx", host(dx), oc.bwd_dx(prob, Y, d["w"], d["grad_out"], sp, pe, sr))
+    ref_dw, ref_dY = oc.bwd_edges(prob, d["x"], Y, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+    close("dw", host(dw), ref_dw)
+    close("dvec", host(dvec), osh.vec_grad_from_sh_grad(deg[1], v64, ref_dY))
+    for u, v in zip((dx, dw, dvec), ctp.conv_tp_bwd(G, x, vt, w, g, deg, ctp.VEC_GIVEN, algo=ctp.ALGO_FRAME)):
+        assert torch.equal(u, v)

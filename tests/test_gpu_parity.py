@@ -924,3 +924,11 @@ def test_double_bwd_edge_vectors(ctp, dev, n, c, L):
     rvec = osh.vec_grad_from_sh_grad(L, v64, rY) + osh.vec_hess_term(L, v64, dY, av)
     for name, got, ref in (("g_x", gx, rx), ("g_w", gw, rw), ("g_vec", gvec, rvec), ("g_grad", gG, rG)):
         close(name, host(got), ref)
+    # with the first backward's dY passed in (Y given): the same bits
+    vt = T(d["vec"], dev)
+    _, _, dYt = ctp.conv_tp_bwd(T(d["grad_out"], dev), T(d["x"], dev), ctp.spherical_harmonics(vt, L),
+                                T(d["w"], dev), g, L, ctp.Y_GIVEN)
+    again = ctp.conv_tp_bwd_bwd_vec(T(d["grad_out"], dev), T(d["x"], dev), vt, T(d["w"], dev), T(ax, dev),
+                                    T(aw, dev), T(av, dev), g, L, dY=dYt)
+    for u, v in zip((gx, gw, gvec, gG), again):
+        assert torch.equal(u, v)
