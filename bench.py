@@ -69,8 +69,8 @@ def run_tag(args):
         tag += "-vec"
     if getattr(args, "frame", False):
         tag += "-frame"
-    if args.workload == "l3mace" and getattr(args, "bwd", "msg") == "sender":
-        tag += "-sender"
+    if args.workload == "l3mace" and getattr(args, "bwd", "msg") != "msg":
+        tag += "-" + args.bwd
     return tag
 
 
@@ -160,14 +160,18 @@ def workload_l3fb(ctp, torch, dev, args):
 
     kb = {"fwd": fwd_bytes(*shp), "bwd": bwd_bytes(*shp)}
     ffma, bfma = fma_per_edge_channel(ctp, L)
-    kf = {"fwd": 2.0 * ffma * shp[1] * 128, "bwd": 2.0 * bfma * shp[1] * 128}
+    # the direct kernels' FMAs (the edge-frame kernels do fewer: no VALU figure for them)
+    kf = None if args.frame else {"fwd": 2.0 * ffma * shp[1] * 128, "bwd": 2.0 * bfma * shp[1] * 128}
     cfg = {"workload": f"lmax=3 conv TP forward+backward, N=16384, C=128, E={shp[1]}, "
                        f"Poisson(45) in-degree, {'vec' if args.vec else 'Y'} given, fp32",
            "n_nodes": shp[0], "n_edges": shp[1], "channels": 128, "lmax": 3,
            "y_mode": "vec" if args.vec else "Y", "paths": shp[6],
            "algo": "edge frame (algo 2), forward and backward" if args.frame else "direct (algo 0)"}
+    # the direct backward issues VALU instructions at 90-96% of the rate the VALU
+    # probe sustains (SQ counters): arithmetic is its bound, HBM the second one
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=shp[1], cfg=cfg,
-                cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=True))
+                cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=True),
+                bound=None if args.frame else "alu")
 
 
 def workload_l3dd(ctp, torch, dev, args):
@@ -247,6 +251,9 @@ def workload_l3mace(ctp, torch, dev, args):
                          device=dev)
         bwd = lambda: ctp.conv_tp_bwd_msg(G, x, y, w, g, L, ctp.Y_GIVEN, dx=dx, dw=dw, dy=dy,  # noqa: E731
                                           variant=V, workspace=ws)
+    elif args.bwd == "atomic":
+        bwd = lambda: ctp.conv_tp_bwd(G, x, y, w, g, L, ctp.Y_GIVEN, dx=dx, dw=dw, dy=dy, variant=V,  # noqa: E731
+                                      algo=ctp.ALGO_ATOMIC)
     else:
         bwd = lambda: ctp.conv_tp_bwd(G, x, y, w, g, L, ctp.Y_GIVEN, dx=dx, dw=dw, dy=dy, variant=V)  # noqa: E731
 
@@ -260,7 +267,8 @@ def workload_l3mace(ctp, torch, dev, args):
     cfg = {"workload": f"MACE variant (natural-parity paths, per-path output slots), lmax=3, N=16384, C=128, "
                        f"E={e}, Poisson(45) in-degree, Y given, fp32",
            "n_nodes": n, "n_edges": e, "channels": c, "lmax": L, "paths": shp[6], "out_dim": shp[5],
-           "backward": "edge messages (conv_tp_bwd_msg)" if args.bwd == "msg" else "sender-major (conv_tp_bwd)"}
+           "backward": {"msg": "edge messages (conv_tp_bwd_msg)", "sender": "sender-major (conv_tp_bwd)",
+                        "atomic": "receiver-major, dx by atomics (conv_tp_bwd algo 1, not reproducible)"}[args.bwd]}
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=e, cfg=cfg, cpu=None)
 
 
@@ -472,6 +480,24 @@ def workload_hbm(ctp, torch, dev, args):
                 edges=0, cfg={"workload": "HBM stream probes: 2 GiB fp32 read, write and copy"}, cpu=None)
 
 
+def measured_valu_ceiling(ctp, torch, dev, iters=20000, reps=5):
+    """fp32 FMA rate (TFLOP/s) the library's VALU probe sustains on this
+    device right after the timed steps: HIP events around single launches on
+    the current stream, best of reps."""
+    sink = torch.zeros(4, device=dev)
+    fmas = ctp.valu_probe(iters, sink)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ctp.valu_probe(iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2.0 * fmas / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
+
+
 def workload_valu(ctp, torch, dev, args):
     """Arithmetic ceiling: the library's fp32 FMA probe (non-packed, eight
     chains per lane, eight waves per SIMD on every CU)."""
@@ -575,8 +601,9 @@ def main():
     ap.add_argument("--vec", action="store_true", help="l3fb with edge vectors instead of Y")
     ap.add_argument("--frame", action="store_true",
                     help="l3fb --vec and water: forward and backward in each edge's frame (algo 2)")
-    ap.add_argument("--bwd", choices=("msg", "sender"), default="msg",
-                    help="l3mace: backward through edge messages (conv_tp_bwd_msg) or sender-major (conv_tp_bwd)")
+    ap.add_argument("--bwd", choices=("msg", "sender", "atomic"), default="msg",
+                    help="l3mace: backward through edge messages (conv_tp_bwd_msg), sender-major (conv_tp_bwd) "
+                         "or receiver-major with dx by atomics (conv_tp_bwd algo 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-nodes", type=int, default=0,
                     help="receivers in the CPU-oracle sample (0: all of them)")
@@ -655,10 +682,13 @@ def main():
         alu = {"achieved": round(tf, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                "frac": round(tf / VALU_PEAK_TFLOPS, 4), "flops": wl["kernel_flops"][dom]}
         if wl.get("bound") == "alu":
-            # arithmetic holds this kernel: the VALU figure is the roofline, HBM the second bound
+            # arithmetic holds this kernel: the VALU figure is the roofline, HBM the second
+            # bound; the probe's rate on this device is the practical VALU ceiling
             hbm = {k: line["roofline"][k] for k in ("achieved", "peak", "unit", "frac")}
+            ceil = measured_valu_ceiling(ctp, torch, dev)
             line["roofline"] = {"bound": "alu", "kernel": dom, **{k: alu[k] for k in ("achieved", "peak", "unit", "frac")},
-                                "traffic": traffic, "flops": alu["flops"], "hbm": hbm}
+                                "traffic": traffic, "flops": alu["flops"], "hbm": hbm,
+                                "measured_ceiling": round(ceil, 2), "frac_of_measured": round(tf / ceil, 4)}
         else:
             line["roofline"]["alu"] = alu
     if wl.get("cpu") and not args.no_cpu_baseline:

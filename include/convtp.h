@@ -68,7 +68,8 @@
  * the same result in either order, so this keeps the guarantee.  The same
  * holds for the channel sums (dY, dvec, g_y) above 512 channels, which two
  * channel tiles of at most 512 channels each add into a zeroed output.  algo
- * 1 (edge-parallel atomics) is not reproducible.
+ * 1 (atomics: edge-parallel forward, receiver-major backward) is not
+ * reproducible.
  */
 #ifndef CONVTP_H
 #define CONVTP_H
@@ -82,7 +83,7 @@ extern "C" {
 enum {
     CTP_OK = 0,
     CTP_EINVAL = 1,        /* null pointer, negative size, bad enum value */
-    CTP_EUNSUPPORTED = 2,  /* degree outside 0..3, channels above 1024, algo 1 in a backward, algo 2
+    CTP_EUNSUPPORTED = 2,  /* degree outside 0..3, channels above 1024, algo 1 outside conv_tp_fwd/bwd, algo 2
                               with Y given, variant 1 or in an entry point other than conv_tp_fwd and
                               conv_tp_bwd, edge vectors where only Y is taken */
     CTP_EALIGN = 3,        /* a feature/weight array not 16-byte aligned, an index array not 4-byte aligned */
@@ -98,7 +99,7 @@ typedef struct conv_tp_problem {
     int32_t l_sh;      /* max degree of Y, 0..3 */
     int32_t l_out;     /* max degree of out, 0..3 (independent of l_in and l_sh) */
     int32_t y_mode;    /* 0: Y[E][D_sh] given; 1: vec[E][3] given, Y evaluated in-kernel */
-    int32_t algo;      /* 0: CSR segmented sum, deterministic; 1: edge-parallel atomics (forward only);
+    int32_t algo;      /* 0: CSR segmented sum, deterministic; 1: fp32 atomics (not reproducible);
                           2: in each edge's own frame (conv_tp_fwd and conv_tp_bwd; y_mode 1, variant 0) */
     int32_t variant;   /* 0: every triangle path, same-l3 paths summed into one block of D_out = (l_out+1)^2;
                           1: MACE's convolution - natural-parity paths only (l1+l2+l3 even; e3j Table 3's
@@ -155,8 +156,12 @@ int32_t conv_tp_fwd(const conv_tp_problem *prob, const float *x, const float *y_
  * z, coupled through the m2 = 0 slice of every path, dx rotated back, and of
  * the harmonic gradient only the m2 = +-1 components (the ones with a gradient
  * across the edge direction there) are formed for dvec.  The same result up
- * to rounding, about 45% fewer FMAs per edge and channel at l = 3.  algo 1 is
- * rejected (CTP_EUNSUPPORTED). */
+ * to rounding, about 45% fewer FMAs per edge and channel at l = 3.  algo 1:
+ * one workgroup per receiver walks its in-edges (grad_out row read once, as
+ * in conv_tp_bwd_msg) and adds each edge's dx contribution into dx[sender]
+ * with fp32 atomics (dx zeroed first): no workspace and no second pass, but
+ * dx is not bitwise reproducible (dw and dY are); the transpose arrays are
+ * still required. */
 int32_t conv_tp_bwd(const conv_tp_problem *prob, const float *grad_out, const float *x, const float *y_or_vec,
                     const float *w, const int32_t *row_ptr, const int32_t *senders, const int32_t *send_ptr,
                     const int32_t *send_perm, const int32_t *send_recv, float *dx, float *dw, float *dy_or_dvec,
@@ -354,7 +359,7 @@ const char *conv_tp_last_error(void);
  * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward), 104 conv_tp_bwd_dy, 105
  * independent degrees, up to 1024 channels in every backward and variant 1
  * in conv_tp_bwd_bwd, 106 conv_tp_bwd_msg_noalloc, 107 conv_tp_valu_probe and algo 2 in
- * conv_tp_bwd, 108 conv_tp_bwd_bwd_vec. */
+ * conv_tp_bwd, 108 conv_tp_bwd_bwd_vec, 109 algo 1 in conv_tp_bwd. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

@@ -319,7 +319,10 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
 
 // ------------------------------------------------------------ K3m: receiver-major backward with edge messages
 
-template <class S, bool VEC>
+// ATOMIC_DX: each edge's message is added into dx[sender] (zeroed first) with
+// fp32 atomics instead of being stored: no workspace and no second pass, but
+// the order of the additions into dx varies from run to run.
+template <class S, bool VEC, bool ATOMIC_DX>
 __global__ void __launch_bounds__(kBwdMaxThreads)
 __attribute__((amdgpu_waves_per_eu(S::V == kVariantSlots ? 2 : kBwdWavesPerEU, 8)))
 k_bwd_recv(int C, const float* __restrict__ G, const float* __restrict__ x, const float* __restrict__ yv,
@@ -377,7 +380,13 @@ k_bwd_recv(int C, const float* __restrict__ G, const float* __restrict__ x, cons
 #pragma unroll
         for (int d = 0; d < 16; ++d) dya[d] = 0.0f;
         edge_backward<S>(sT[buf], xv, gv, wv, make_row(dw + e * P * C, (long)P * C), voff, C, mx, dya);
-        {
+        if constexpr (ATOMIC_DX) {
+            if (c0 < C) {
+                float* o = msg + (long)senders[e] * D1 * C + c0;   // msg = dx here
+#pragma unroll
+                for (int d = 0; d < D1; ++d) unsafeAtomicAdd(o + (long)d * C, mx[d]);
+            }
+        } else {
             const rsrc_t mr = make_row(msg + e * D1 * C, (long)D1 * C);
 #pragma unroll
             for (int d = 0; d < D1; ++d) {
@@ -444,19 +453,31 @@ hipError_t bwd_launch(const LaunchArgs& a, hipStream_t st) {
 
 // Pass 1 of the message backward (pass 2, the per-sender sums, is launched by
 // the caller): dw, dY and msg[E][D1][C].
-template <class S>
-hipError_t bwd_recv_launch(const LaunchArgs& a, float* msg, hipStream_t st) {
+template <class S, bool ATOMIC_DX>
+hipError_t recv_launch(const LaunchArgs& a, float* msg, hipStream_t st) {
     const BwdTiles t = bwd_tiles(a.C);
     zero_dy_for_tiles(a, t.tiles, S::D2, st);
+    if (ATOMIC_DX) hipLaunchKernelGGL(k_fill0, dim3(1024), dim3(256), 0, st, msg, (long)a.n_nodes * S::D1 * a.C);
     if (a.n_edges == 0) return hipGetLastError();
     const dim3 grid(a.n_nodes, t.tiles), block(64 * t.waves);
     if (a.vec_mode)
-        hipLaunchKernelGGL((k_bwd_recv<S, true>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w, a.row_ptr,
-                           a.senders, msg, a.dw, a.dy, (int)(t.tiles > 1));
+        hipLaunchKernelGGL((k_bwd_recv<S, true, ATOMIC_DX>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+                           a.row_ptr, a.senders, msg, a.dw, a.dy, (int)(t.tiles > 1));
     else
-        hipLaunchKernelGGL((k_bwd_recv<S, false>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w, a.row_ptr,
-                           a.senders, msg, a.dw, a.dy, (int)(t.tiles > 1));
+        hipLaunchKernelGGL((k_bwd_recv<S, false, ATOMIC_DX>), grid, block, 0, st, a.C, a.grad, a.x, a.y, a.w,
+                           a.row_ptr, a.senders, msg, a.dw, a.dy, (int)(t.tiles > 1));
     return hipGetLastError();
+}
+
+template <class S>
+hipError_t bwd_recv_launch(const LaunchArgs& a, float* msg, hipStream_t st) {
+    return recv_launch<S, false>(a, msg, st);
+}
+
+// algo 1: receiver-major, messages added into dx with atomics.
+template <class S>
+hipError_t bwd_atomic_launch(const LaunchArgs& a, hipStream_t st) {
+    return recv_launch<S, true>(a, a.dx, st);
 }
 
 }  // namespace conv

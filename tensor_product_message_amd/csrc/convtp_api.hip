@@ -107,7 +107,6 @@ int bwd_args(const conv_tp_problem* prob, const float* grad_out, const float* x,
              ctp::LaunchArgs* out) {
     Shape& s = *sp;
     if (int r = check_problem(prob, &s)) return r;
-    if (prob->algo == 1) return fail(CTP_EUNSUPPORTED, "the backward has no atomic variant (algo 1)");
     if (prob->algo == 2 && (prob->y_mode != 1 || prob->variant != ctp::kVariantSummed))
         return fail(CTP_EUNSUPPORTED, "algo 2 (edge frame) needs edge vectors (y_mode 1) and variant 0");
     if (int r = need(grad_out, s.N * s.D3 * s.C, 16, "grad_out")) return r;
@@ -210,7 +209,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 108; }
+int32_t conv_tp_version(void) { return 109; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 

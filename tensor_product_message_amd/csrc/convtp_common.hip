@@ -223,6 +223,9 @@ hipError_t launch_bwd(const LaunchArgs& a, hipStream_t st) {
     if (a.algo == 2)
         return by_triple(triple_key(a.l_in, a.l_sh, a.l_out),
                          [&]<int A, int B, int C>() { return Triple<A, B, C>::bwd_frame(a, st); });
+    if (a.algo == 1)
+        return by_triple(triple_key(a.l_in, a.l_sh, a.l_out),
+                         [&]<int A, int B, int C>() { return Triple<A, B, C>::bwd_atomic(a, st); });
     return by_triple(triple_key(a.l_in, a.l_sh, a.l_out),
                      [&]<int A, int B, int C>() { return Triple<A, B, C>::bwd(a, st); });
 }

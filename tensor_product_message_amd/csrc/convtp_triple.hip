@@ -58,6 +58,12 @@ hipError_t Triple<L1, L2, L3>::bwd(const LaunchArgs& a, hipStream_t st) {
 }
 
 template <int L1, int L2, int L3>
+hipError_t Triple<L1, L2, L3>::bwd_atomic(const LaunchArgs& a, hipStream_t st) {
+    if (a.variant == kVariantSlots) return conv::bwd_atomic_launch<Spec<L1, L2, L3, kVariantSlots>>(a, st);
+    return conv::bwd_atomic_launch<Spec<L1, L2, L3, kVariantSummed>>(a, st);
+}
+
+template <int L1, int L2, int L3>
 hipError_t Triple<L1, L2, L3>::bwd_frame(const LaunchArgs& a, hipStream_t st) {
     return conv::frame_bwd_launch<Spec<L1, L2, L3, kVariantSummed>>(a, st);
 }

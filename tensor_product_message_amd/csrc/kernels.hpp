@@ -10,7 +10,7 @@ namespace ctp {
 struct LaunchArgs {
     int l_in, l_sh, l_out; // degrees of x, Y and out
     int n_nodes, n_edges, C;
-    int algo;              // 0: CSR deterministic, 1: edge-parallel atomic (forward), 2: edge frame (edge vectors)
+    int algo;              // 0: CSR deterministic, 1: atomics (forward: edge-parallel; backward: into dx), 2: edge frame
     int vec_mode;          // 0: Y[E][D2] given, 1: vec[E][3] given
     int variant;           // 0: all paths, same-l3 sums; 1: natural-parity paths, one output slot each
     const float* x;        // [N][D1][C]
@@ -52,6 +52,7 @@ struct Triple {
     static hipError_t fwd(const LaunchArgs& a, hipStream_t st);          // algo 0 and 1
     static hipError_t fwd_frame(const LaunchArgs& a, hipStream_t st);    // algo 2, variant 0
     static hipError_t bwd(const LaunchArgs& a, hipStream_t st);          // sender-major
+    static hipError_t bwd_atomic(const LaunchArgs& a, hipStream_t st);   // algo 1, receiver-major, atomics into dx
     static hipError_t bwd_frame(const LaunchArgs& a, hipStream_t st);    // algo 2, edge vectors, variant 0
     static hipError_t bwd_recv(const LaunchArgs& a, float* msg, hipStream_t st);   // message pass 1
     static hipError_t bwd_dy(const LaunchArgs& a, hipStream_t st);

@@ -199,7 +199,8 @@ def conv_tp_fwd(x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN, 
 def conv_tp_bwd(grad_out, x, y_or_vec, w, graph: Graph, lmax: int, y_mode: int = Y_GIVEN,
                 dx=None, dw=None, dy=None, variant: int = SUMMED, algo: int = ALGO_CSR):
     """(dx, dw, dY or dvec) for upstream gradient grad_out (see include/convtp.h);
-    algo ALGO_FRAME computes it in each edge's frame (edge vectors)."""
+    algo ALGO_FRAME computes it in each edge's frame (edge vectors); ALGO_ATOMIC walks
+    receivers and adds dx with atomics (dx not bitwise reproducible)."""
     n, e, c = _shapes(x, y_or_vec, w, graph, lmax, y_mode, variant)
     _want(grad_out, "grad_out", (n, out_dim(lmax, variant), c), device=x.device)
     send_ptr, send_perm, send_recv = graph.transpose

@@ -65,6 +65,7 @@ def test_run_tags_keep_modes_apart(tmp_path, monkeypatch):
     assert bench.run_tag(A(vec=True)) == "l3fb-vec"
     assert bench.run_tag(A(vec=True, frame=True)) == "l3fb-vec-frame"
     assert bench.run_tag(A(workload="l3mace", bwd="sender")) == "l3mace-sender"
+    assert bench.run_tag(A(workload="l3mace", bwd="atomic")) == "l3mace-atomic"
     # a record of the Y-given run is never reported for the edge-vector run
     rec = dict(workload="l3fb", tag="l3fb", kernel="bwd", source_sha=bench.kernel_sources_sha("l3fb"),
                bytes_per_launch=123)

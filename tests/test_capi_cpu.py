@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 108
+    assert L.conv_tp_version() == 109
 
 
 def test_paths_match_oracle(capi):
@@ -158,11 +158,14 @@ def test_every_degree_triple_and_channel_count_is_accepted(capi, deg, channels):
 
 
 def test_bwd_rejections(capi):
-    assert _bwd(capi, _prob(capi, algo=1)) == capi.CTP_EUNSUPPORTED
     assert _bwd(capi, _prob(capi, channels=1025)) == capi.CTP_EUNSUPPORTED
+    assert _bwd(capi, _prob(capi, algo=1, channels=1025)) == capi.CTP_EUNSUPPORTED
+    assert _bwd(capi, _prob(capi, algo=3)) == capi.CTP_EINVAL
+    for algo in (0, 1):
+        p = _prob(capi, algo=algo)
+        for k in ("g", "x", "y", "w", "rp", "s", "sp", "pe", "sr", "dx", "dw", "dy"):
+            assert _bwd(capi, p, **{k: NUL}) == capi.CTP_EINVAL, (algo, k)
     p = _prob(capi)
-    for k in ("g", "x", "y", "w", "rp", "s", "sp", "pe", "sr", "dx", "dw", "dy"):
-        assert _bwd(capi, p, **{k: NUL}) == capi.CTP_EINVAL, k
     assert _bwd(capi, p, dw=MIS) == capi.CTP_EALIGN
     assert _bwd(capi, p, g=MIS) == capi.CTP_EALIGN
 

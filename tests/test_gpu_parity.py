@@ -757,7 +757,8 @@ def test_frame_forward_water_box(ctp, dev):
 
 def run_msg(ctp, dev, d, L, y_mode, variant, ws=None):
     """conv_tp_bwd_msg against the oracle (dx, dw, dY) and against conv_tp_bwd
-    (dw and dY bitwise: the same per-edge arithmetic)."""
+    (dw and dY bitwise: the same per-edge arithmetic); conv_tp_bwd algo 1 (the
+    receiver-major pass with atomics into dx) likewise."""
     n, e = d["n_nodes"], d["n_edges"]
     prob = oc.Problem(L, L, L, variant=variant)
     vec = d["vec"]
@@ -778,6 +779,10 @@ def run_msg(ctp, dev, d, L, y_mode, variant, ws=None):
         close("dvec", host(dy), osh.vec_grad_from_sh_grad(L, vec.astype(np.float64), dY_ref), nonzero=e > 0 and L > 0)
     dx0, dw0, dy0 = ctp.conv_tp_bwd(G, x, yv, w, g, L, y_mode, variant=variant)
     assert torch.equal(dw, dw0) and torch.equal(dy, dy0)
+    # algo 1: the same receiver-major pass with dx added by atomics (dw, dY the same bits)
+    dx1, dw1, dy1 = ctp.conv_tp_bwd(G, x, yv, w, g, L, y_mode, variant=variant, algo=ctp.ALGO_ATOMIC)
+    close("dx (algo 1)", host(dx1), oc.bwd_dx(prob, Yref, d["w"], d["grad_out"], sp, pe, sr), nonzero=e > 0)
+    assert torch.equal(dw1, dw) and torch.equal(dy1, dy)
 
 
 @pytest.mark.parametrize("n,c,L", [(90, 16, 1), (150, 48, 2), (100, 128, 3), (60, 192, 3), (40, 96, 0),
