@@ -86,6 +86,9 @@ def check_all(ctp, dev, deg, n, c, variant, y_mode, seed, msg=True):
     runs = [ctp.conv_tp_bwd(G, x, yv, w, g, deg, y_mode, variant=variant)]
     if msg:
         runs.append(ctp.conv_tp_bwd_msg(G, x, yv, w, g, deg, y_mode, variant=variant))
+        # algo 1: receiver-major with dx added by atomics; dw and dY the same bits as the message pass
+        runs.append(ctp.conv_tp_bwd(G, x, yv, w, g, deg, y_mode, variant=variant, algo=ctp.ALGO_ATOMIC))
+        assert torch.equal(runs[2][1], runs[1][1]) and torch.equal(runs[2][2], runs[1][2])
     for k, (dx, dw, dy) in enumerate(runs):
         close(f"dx[{k}]", host(dx), ref_dx)
         close(f"dw[{k}]", host(dw), ref_dw)
@@ -129,6 +132,52 @@ def test_degree_triples_double_bwd(ctp, dev, deg, variant):
                                      d["senders"])
     for name, got, want in zip(("g_x", "g_w", "g_y", "g_grad"), res, ref):
         close(name, host(got), want)
+
+
+@pytest.mark.parametrize("deg", [(0, 3, 3), (3, 2, 1), (1, 1, 2)])
+@pytest.mark.parametrize("variant", [0, 1])
+def test_degree_triples_double_bwd_edge_vectors(ctp, dev, deg, variant):
+    """conv_tp_bwd_bwd_vec against the oracle, with dY recomputed and with the
+    first backward's dY passed in (the same bits)."""
+    prob, d = workload(deg, 50, 64, variant, seed=17 + variant)
+    n, l_sh = d["n_nodes"], deg[1]
+    rng = np.random.default_rng(7)
+    ax = rng.standard_normal(d["x"].shape, dtype=np.float32)
+    aw = rng.standard_normal(d["w"].shape, dtype=np.float32)
+    av = rng.standard_normal((d["n_edges"], 3), dtype=np.float32)
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    G, x, w, vt = T(d["grad_out"], dev), T(d["x"], dev), T(d["w"], dev), T(d["vec"], dev)
+    args = (G, x, vt, w, T(ax, dev), T(aw, dev), T(av, dev), g, deg)
+    res = ctp.conv_tp_bwd_bwd_vec(*args, variant=variant)
+    v64 = d["vec"].astype(np.float64)
+    Y = osh.real_sh(l_sh, v64)
+    aY = osh.real_sh_jvp(l_sh, v64, av)
+    rx, rw, rY, rG = oc.materialised_double_bwd(prob, d["x"], Y, d["w"], d["grad_out"], ax, aw, aY,
+                                                d["row_ptr"], d["senders"])
+    _, _, dY = oc.materialised_bwd(prob, d["x"], Y, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
+    rvec = osh.vec_grad_from_sh_grad(l_sh, v64, rY) + osh.vec_hess_term(l_sh, v64, dY, av)
+    for name, got, want in zip(("g_x", "g_w", "g_vec", "g_grad"), res, (rx, rw, rvec, rG)):
+        close(name, host(got), want)
+    dYt = ctp.conv_tp_bwd(G, x, ctp.spherical_harmonics(vt, l_sh), w, g, deg, ctp.Y_GIVEN, variant=variant)[2]
+    for u, v in zip(res, ctp.conv_tp_bwd_bwd_vec(*args, variant=variant, dY=dYt)):
+        assert torch.equal(u, v)
+
+
+def test_double_bwd_edge_vectors_nodes_without_edges(ctp, dev):
+    """Nodes but no edges: g_x and g_grad come out zero, the per-edge outputs
+    are empty, with and without dY."""
+    n, c, deg = 12, 64, (2, 2, 2)
+    prob = oc.Problem(*deg)
+    g = ctp.Graph(n, torch.zeros(n + 1, dtype=torch.int32, device=dev), torch.zeros(0, dtype=torch.int32, device=dev))
+    x = torch.randn(n, prob.D1, c, device=dev)
+    G = torch.randn(n, prob.D3, c, device=dev)
+    w = torch.zeros(0, prob.P, c, device=dev)
+    v = torch.zeros(0, 3, device=dev)
+    for dY in (None, torch.zeros(0, 9, device=dev)):
+        gx, gw, gv, gG = ctp.conv_tp_bwd_bwd_vec(G, x, v, w, torch.randn_like(x), w.clone(), v.clone(), g, deg,
+                                                 dY=dY)
+        assert gw.numel() == 0 and gv.numel() == 0
+        assert torch.count_nonzero(gx) == 0 and torch.count_nonzero(gG) == 0
 
 
 @pytest.mark.parametrize("deg", [(0, 3, 3), (2, 1, 3), (3, 3, 3)])
