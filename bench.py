@@ -567,6 +567,7 @@ def cpu_baseline(spec, sample_nodes):
     what = "forward + backward (dx, dw, dY)" if fb else "forward"
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": nt, "kind": "oracle",
             "edges_per_s": round(edges_per_s, 1), "seconds": round(t, 2),
+            "forward_seconds": round(t_fwd, 2), "backward_seconds": round(t_bwd, 2),
             "sample": f"{what} over the {e_sample} in-edges of the first {len(rows)} receivers "
                       f"({e_sample / E:.1%} of the edges), fp64 C edge loop, {nt} OpenMP threads; "
                       "GB/s = edges/s x the step's algorithmic bytes per edge"}
