@@ -9,7 +9,9 @@ nodes, C = 128 channels (N*C = 2^21), Poisson(45) in-degrees, Y given,
 forward (CSR, deterministic) + backward (dx, dw, dY).  Other workloads:
 `l2fwd` (lmax 2, N = 32768, forward), `sweepC` (lmax 2, N = 2^22/C, forward,
 CSR and atomic timed, C in 64..1024), `water` (1503 atoms, 83,325 edges,
-two lmax-3 layers forward + backward to edge vectors), `tiny`.
+two lmax-3 layers forward + backward to edge vectors, in each edge's frame;
+`--direct` for the direct kernels), `tiny`, and the diagnostics listed
+under --workload.
 
 Throughput is algorithmic bytes / time (the byte model counts every array
 the method must touch once: w, Y or vec, index arrays, x and G once, outputs
@@ -67,8 +69,10 @@ def run_tag(args):
     tag = args.workload
     if getattr(args, "vec", False):
         tag += "-vec"
-    if getattr(args, "frame", False):
+    if getattr(args, "frame", False) and args.workload != "water":
         tag += "-frame"
+    if args.workload == "water" and getattr(args, "direct", False):
+        tag += "-direct"
     if args.workload == "l3mace" and getattr(args, "bwd", "msg") != "msg":
         tag += "-" + args.bwd
     return tag
@@ -359,7 +363,9 @@ def workload_water(ctp, torch, dev, args):
     dv1, dv2 = torch.empty_like(v), torch.empty_like(v)
     torch.cuda.synchronize()
 
-    fwd_algo = ctp.ALGO_FRAME if args.frame else ctp.ALGO_CSR
+    # edge vectors: the edge-frame kernels by default (the same result up to
+    # rounding, fewer FMAs); --direct times the direct kernels
+    fwd_algo = ctp.ALGO_CSR if args.direct else ctp.ALGO_FRAME
 
     def step(t):
         t.run("fwd1", lambda: ctp.conv_tp_fwd(x0, v, w1, g, L, y_mode, fwd_algo, out=h1))
@@ -373,7 +379,7 @@ def workload_water(ctp, torch, dev, args):
     cfg = {"workload": f"water-box-shaped step: 1503 atoms, {E} edges (10% zero-weight padding), "
                        "C=128, lmax=3, vec given, two layers forward + backward to edge vectors, fp32",
            "n_nodes": n, "n_edges": E, "channels": 128, "lmax": 3, "layers": 2,
-           "algo": "edge frame (algo 2), forward and backward" if args.frame else "direct (algo 0)"}
+           "algo": "direct (algo 0)" if args.direct else "edge frame (algo 2), forward and backward"}
     return dict(step=step, kernel_bytes=kb, dominant="bwd1", edges=E, cfg=cfg, cpu=None)
 
 
@@ -601,7 +607,9 @@ def main():
     ap.add_argument("--gather-nodes", type=int, default=64, help="gather only: nodes the row gathers touch")
     ap.add_argument("--vec", action="store_true", help="l3fb with edge vectors instead of Y")
     ap.add_argument("--frame", action="store_true",
-                    help="l3fb --vec and water: forward and backward in each edge's frame (algo 2)")
+                    help="l3fb --vec: forward and backward in each edge's frame (algo 2; the water box's default)")
+    ap.add_argument("--direct", action="store_true",
+                    help="water: the direct kernels (algo 0) instead of the edge frame")
     ap.add_argument("--bwd", choices=("msg", "sender", "atomic"), default="msg",
                     help="l3mace: backward through edge messages (conv_tp_bwd_msg), sender-major (conv_tp_bwd) "
                          "or receiver-major with dx by atomics (conv_tp_bwd algo 1)")

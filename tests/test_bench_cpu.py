@@ -60,12 +60,15 @@ def test_traffic_records_follow_the_sources(tmp_path, monkeypatch):
 
 def test_run_tags_keep_modes_apart(tmp_path, monkeypatch):
     import argparse
-    A = lambda **kw: argparse.Namespace(**{**dict(workload="l3fb", vec=False, frame=False, bwd="msg"), **kw})  # noqa: E731
+    A = lambda **kw: argparse.Namespace(**{**dict(workload="l3fb", vec=False, frame=False, bwd="msg",  # noqa: E731
+                                                  direct=False), **kw})
     assert bench.run_tag(A()) == "l3fb"
     assert bench.run_tag(A(vec=True)) == "l3fb-vec"
     assert bench.run_tag(A(vec=True, frame=True)) == "l3fb-vec-frame"
     assert bench.run_tag(A(workload="l3mace", bwd="sender")) == "l3mace-sender"
     assert bench.run_tag(A(workload="l3mace", bwd="atomic")) == "l3mace-atomic"
+    assert bench.run_tag(A(workload="water")) == bench.run_tag(A(workload="water", frame=True)) == "water"
+    assert bench.run_tag(A(workload="water", direct=True)) == "water-direct"
     # a record of the Y-given run is never reported for the edge-vector run
     rec = dict(workload="l3fb", tag="l3fb", kernel="bwd", source_sha=bench.kernel_sources_sha("l3fb"),
                bytes_per_launch=123)
