@@ -471,19 +471,26 @@ def workload_node(ctp, torch, dev, args):
 
 
 def workload_hbm(ctp, torch, dev, args):
-    """Practical HBM ceilings: the library's stream probes (16-byte non-temporal
-    read, write and copy of 2 GiB), the access shape of the kernels' edge streams."""
+    """Practical HBM ceilings: the library's stream probes (non-temporal read,
+    write and copy of 2 GiB, grid-stride), with 16-byte accesses per lane and
+    with 4-byte ones (`*_b32`: the width of the kernels' row accesses)."""
     n = (1 << 31) // 4
     src = torch.ones(n, device=dev)
     dst = torch.empty_like(src)
+    D = ctp.STREAM_DWORD
 
     def step(t):
         t.run("read", lambda: ctp.stream_probe(ctp.STREAM_READ, src, dst))
         t.run("write", lambda: ctp.stream_probe(ctp.STREAM_WRITE, None, dst))
         t.run("copy", lambda: ctp.stream_probe(ctp.STREAM_COPY, src, dst))
+        t.run("read_b32", lambda: ctp.stream_probe(ctp.STREAM_READ + D, src, dst))
+        t.run("write_b32", lambda: ctp.stream_probe(ctp.STREAM_WRITE + D, None, dst))
+        t.run("copy_b32", lambda: ctp.stream_probe(ctp.STREAM_COPY + D, src, dst))
 
-    return dict(step=step, kernel_bytes={"read": 4 * n, "write": 4 * n, "copy": 8 * n}, dominant="copy",
-                edges=0, cfg={"workload": "HBM stream probes: 2 GiB fp32 read, write and copy"}, cpu=None)
+    kb = {"read": 4 * n, "write": 4 * n, "copy": 8 * n, "read_b32": 4 * n, "write_b32": 4 * n, "copy_b32": 8 * n}
+    return dict(step=step, kernel_bytes=kb, dominant="copy", edges=0,
+                cfg={"workload": "HBM stream probes: 2 GiB fp32 read, write and copy, 16- and 4-byte accesses"},
+                cpu=None)
 
 
 def measured_valu_ceiling(ctp, torch, dev, iters=20000, reps=5):

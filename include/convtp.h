@@ -335,7 +335,9 @@ int32_t conv_tp_node_bwd(const conv_tp_node_problem *prob, const float *grad_out
 /* Measurement helper, not part of the operation: plain HBM streams shaped
  * like the kernels' edge streams (16-byte non-temporal accesses, grid-stride
  * loop).  kind 0 reads src[n_floats] (dst receives at most one float, only
- * for a non-finite input), 1 writes dst[n_floats], 2 copies src to dst.  They
+ * for a non-finite input), 1 writes dst[n_floats], 2 copies src to dst;
+ * kinds 3, 4 and 5 are the same streams with 4-byte accesses per lane (the
+ * width of the kernels' one-channel-per-lane row accesses).  They
  * measure the bandwidth this device sustains for each traffic mix, against
  * which the kernels' fractions of the data-sheet HBM peak are read (e3j
  * abstract: throughput quoted as a fraction of maximum HBM bandwidth).
@@ -359,7 +361,8 @@ const char *conv_tp_last_error(void);
  * conv_tp_bwd_msg, 103 algo 2 (edge-frame forward), 104 conv_tp_bwd_dy, 105
  * independent degrees, up to 1024 channels in every backward and variant 1
  * in conv_tp_bwd_bwd, 106 conv_tp_bwd_msg_noalloc, 107 conv_tp_valu_probe and algo 2 in
- * conv_tp_bwd, 108 conv_tp_bwd_bwd_vec, 109 algo 1 in conv_tp_bwd. */
+ * conv_tp_bwd, 108 conv_tp_bwd_bwd_vec, 109 algo 1 in conv_tp_bwd, 110 4-byte stream
+ * probes. */
 int32_t conv_tp_version(void);
 
 #ifdef __cplusplus

@@ -209,7 +209,7 @@ int host_coupling(int l1, int l2, int l3, double* out) {
 
 extern "C" {
 
-int32_t conv_tp_version(void) { return 109; }
+int32_t conv_tp_version(void) { return 110; }
 
 const char* conv_tp_last_error(void) { return g_last_error.c_str(); }
 
@@ -622,12 +622,14 @@ int32_t conv_tp_node_bwd(const conv_tp_node_problem* prob, const float* grad_out
 }
 
 int32_t conv_tp_stream_probe(int32_t kind, const float* src, float* dst, int64_t n_floats, void* stream) {
-    if (kind < 0 || kind > 2) return fail(CTP_EINVAL, "kind = %d not 0 (read), 1 (write) or 2 (copy)", kind);
+    if (kind < 0 || kind > 5)
+        return fail(CTP_EINVAL, "kind = %d not 0..5 (read, write, copy; 3..5 the same with 4-byte accesses)", kind);
     if (n_floats < 0 || n_floats % 4 != 0) return fail(CTP_EINVAL, "n_floats = %lld must be a non-negative multiple of 4",
                                                        (long long)n_floats);
-    if (kind != 1)
+    const int base_kind = kind % 3;
+    if (base_kind != 1)
         if (int r = need(src, n_floats, 16, "src")) return r;
-    if (int r = need(dst, kind == 0 ? (n_floats > 0 ? 1 : 0) : n_floats, 16, "dst")) return r;
+    if (int r = need(dst, base_kind == 0 ? (n_floats > 0 ? 1 : 0) : n_floats, 16, "dst")) return r;
     if (n_floats == 0) return ok();
     return hip_status(ctp::launch_stream_probe(kind, src, dst, (long)n_floats, static_cast<hipStream_t>(stream)),
                       "stream probe launch");

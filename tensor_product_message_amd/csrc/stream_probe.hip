@@ -1,5 +1,5 @@
-// Plain HBM streams (read, write, copy) with the access shape and cache policy
-// of the conv kernels' edge streams: 16-byte accesses, non-temporal, a
+// Plain HBM streams (read, write, copy) with the cache policy of the conv
+// kernels' edge streams: non-temporal, 16-byte or 4-byte accesses per lane, a
 // grid-stride loop (4096 workgroups for reads, 16384 for writes and copies,
 // the best of a sweep on MI355X).  They give the bandwidth this
 // device actually sustains for each traffic mix, the practical ceiling next to
@@ -53,6 +53,51 @@ __global__ void __launch_bounds__(kProbeThreads) k_stream_copy(const f4* __restr
     for (; i < n4; i += bd) __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
 }
 
+// The same three streams with 4-byte accesses per lane (one dword: 256 bytes
+// per wave-wide instruction), the width of the conv kernels' one-channel-per-
+// lane row accesses.  Reads and the copy keep kDwordDepth loads in flight per
+// lane, as many bytes per lane as four 16-byte loads.
+constexpr int kDwordDepth = 16;
+
+__global__ void __launch_bounds__(kProbeThreads) k_stream_read1(const float* __restrict__ a, float* __restrict__ sink,
+                                                                long n) {
+    const long bd = blockDim.x;
+    const long st = (long)gridDim.x * bd * kDwordDepth;
+    float s[kDwordDepth];
+#pragma unroll
+    for (int u = 0; u < kDwordDepth; ++u) s[u] = 0.0f;
+    long i = (long)blockIdx.x * bd * kDwordDepth + threadIdx.x;
+    for (; i + (kDwordDepth - 1) * bd < n; i += st) {
+#pragma unroll
+        for (int u = 0; u < kDwordDepth; ++u) s[u] += __builtin_nontemporal_load(a + i + u * bd);
+    }
+    for (; i < n; i += bd) s[0] += __builtin_nontemporal_load(a + i);
+    float t = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kDwordDepth; ++u) t += s[u];
+    if (t != t && threadIdx.x == 0) sink[0] = t;
+}
+
+__global__ void __launch_bounds__(kProbeThreads) k_stream_write1(float* __restrict__ b, long n) {
+    const long st = (long)gridDim.x * blockDim.x;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += st) __builtin_nontemporal_store(1.0f, b + i);
+}
+
+__global__ void __launch_bounds__(kProbeThreads) k_stream_copy1(const float* __restrict__ a, float* __restrict__ b,
+                                                                long n) {
+    const long bd = blockDim.x;
+    const long st = (long)gridDim.x * bd * kDwordDepth;
+    long i = (long)blockIdx.x * bd * kDwordDepth + threadIdx.x;
+    for (; i + (kDwordDepth - 1) * bd < n; i += st) {
+        float v[kDwordDepth];
+#pragma unroll
+        for (int u = 0; u < kDwordDepth; ++u) v[u] = __builtin_nontemporal_load(a + i + u * bd);
+#pragma unroll
+        for (int u = 0; u < kDwordDepth; ++u) __builtin_nontemporal_store(v[u], b + i + u * bd);
+    }
+    for (; i < n; i += bd) __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
+}
+
 // Eight independent FMA chains per lane (enough to cover the FMA latency),
 // non-packed fp32; the result is consumed by a store that no finite value
 // takes.  Every workgroup runs the same work: kValuBlocks x 256 threads x
@@ -95,6 +140,9 @@ hipError_t launch_stream_probe(int kind, const float* src, float* dst, long n_fl
             hipLaunchKernelGGL(k_stream_copy, wgrid, block, 0, st, reinterpret_cast<const f4*>(src),
                                reinterpret_cast<f4*>(dst), n4);
             break;
+        case 3: hipLaunchKernelGGL(k_stream_read1, rgrid, block, 0, st, src, dst, n_floats); break;
+        case 4: hipLaunchKernelGGL(k_stream_write1, wgrid, block, 0, st, dst, n_floats); break;
+        case 5: hipLaunchKernelGGL(k_stream_copy1, wgrid, block, 0, st, src, dst, n_floats); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

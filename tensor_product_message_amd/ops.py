@@ -364,12 +364,14 @@ def node_tp_bwd(grad_out, x, y, w, lmax: int, dx=None, dy=None, dw=None):
 
 
 STREAM_READ, STREAM_WRITE, STREAM_COPY = 0, 1, 2
+STREAM_DWORD = 3   # added to a kind: the same stream with 4-byte accesses per lane
 
 
 def stream_probe(kind: int, src, dst):
     """HBM stream probe (measurement only): kind STREAM_READ reads src,
-    STREAM_WRITE writes dst, STREAM_COPY copies src into dst."""
-    t = dst if kind == STREAM_WRITE else src
+    STREAM_WRITE writes dst, STREAM_COPY copies src into dst (16-byte
+    accesses per lane; kind + STREAM_DWORD: 4-byte accesses)."""
+    t = dst if kind % 3 == STREAM_WRITE else src
     n = t.numel()
     for name, a in (("src", src), ("dst", dst)):
         if a is not None:

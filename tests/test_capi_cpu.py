@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(capi):
     assert set(declared) == set(capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.conv_tp_version() == 109
+    assert L.conv_tp_version() == 110
 
 
 def test_paths_match_oracle(capi):
@@ -352,7 +352,11 @@ def test_other_entry_points_validate(capi):
     assert L.conv_tp_build_transpose(4, 3, A, MIS, A, A, ctypes.c_void_p(0x10001), NUL) == capi.CTP_EALIGN
     assert L.conv_tp_check_graph(4, 3, A, A, None, NUL) == capi.CTP_EINVAL
     assert L.conv_tp_check_graph(4, -3, A, A, None, NUL) == capi.CTP_EINVAL
-    assert L.conv_tp_stream_probe(3, A, A2, 16, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(6, A, A2, 16, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(-1, A, A2, 16, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(5, NUL, A2, 16, NUL) == capi.CTP_EINVAL
+    assert L.conv_tp_stream_probe(4, NUL, MIS, 16, NUL) == capi.CTP_EALIGN
+    assert L.conv_tp_stream_probe(3, A, A2, 0, NUL) == capi.CTP_OK
     assert L.conv_tp_stream_probe(2, A, A2, 18, NUL) == capi.CTP_EINVAL
     assert L.conv_tp_stream_probe(2, NUL, A2, 16, NUL) == capi.CTP_EINVAL
     assert L.conv_tp_stream_probe(1, NUL, NUL, 16, NUL) == capi.CTP_EINVAL

@@ -523,6 +523,16 @@ def test_stream_probes(ctp, dev):
     assert float(sink.abs().sum()) == 0.0
     assert torch.equal(dst[:8].cpu(), torch.tensor([1.0, 2.0, 3.0, 4.0] * 2))
     assert bool((dst.view(-1, 4) == torch.tensor([1.0, 2.0, 3.0, 4.0], device=dev)).all())
+    # the 4-byte-access variants
+    dst.zero_()
+    ctp.stream_probe(ctp.STREAM_COPY + ctp.STREAM_DWORD, src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    ctp.stream_probe(ctp.STREAM_READ + ctp.STREAM_DWORD, src, sink)
+    ctp.stream_probe(ctp.STREAM_WRITE + ctp.STREAM_DWORD, None, dst)
+    torch.cuda.synchronize()
+    assert float(sink.abs().sum()) == 0.0
+    assert bool((dst == 1.0).all())
 
 
 # ------------------------------------------------------------ VJP of the VJP (Y given)
