@@ -171,8 +171,9 @@ def workload_l3fb(ctp, torch, dev, args):
            "n_nodes": shp[0], "n_edges": shp[1], "channels": 128, "lmax": 3,
            "y_mode": "vec" if args.vec else "Y", "paths": shp[6],
            "algo": "edge frame (algo 2), forward and backward" if args.frame else "direct (algo 0)"}
-    # the direct backward issues VALU instructions at 90-96% of the rate the VALU
-    # probe sustains (SQ counters): arithmetic is its bound, HBM the second one
+    # the direct backward issues VALU instructions at about 0.9 of the rate the
+    # VALU probe sustains (SQ counters), the unit nearest its ceiling; its HBM
+    # streams, a little further from theirs, are reported beside it
     return dict(step=step, kernel_bytes=kb, kernel_flops=kf, dominant="bwd", edges=shp[1], cfg=cfg,
                 cpu=dict(kind="poisson", d=d, L=L, y_mode=y_mode, shp=shp, fb=True),
                 bound=None if args.frame else "alu")
