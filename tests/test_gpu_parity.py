@@ -226,6 +226,58 @@ def test_hip_graph_replays_frame_and_dy(ctp, dev):
         assert torch.equal(out, ref[0]) and torch.equal(dy, ref[1]), k
 
 
+def test_hip_graph_replays_frame_bwd_atomic_bwd_and_vec_double_bwd(ctp, dev):
+    """The edge-frame backward (small-grid split, dx zero fill), the atomic
+    backward (algo 1, dx zero fill) and the one-call edge-vector double
+    backward (workspace, first backward's dY given), captured in one HIP graph
+    and replayed three times: every output equals the eager run bitwise,
+    except the atomic backward's dx (additions in any order: to tolerance)."""
+    L, n, c = 3, 300, 128
+    d = gen.poisson_small(n, c, L, mean_deg=12.0, seed=78)
+    e = d["n_edges"]
+    g = ctp.Graph(n, T(d["row_ptr"], dev), T(d["senders"], dev))
+    x, w, G, v = T(d["x"], dev), T(d["w"], dev), T(d["grad_out"], dev), T(d["vec"], dev)
+    rng = np.random.default_rng(5)
+    ax, aw = T(rng.standard_normal(d["x"].shape, dtype=np.float32), dev), T(rng.standard_normal(d["w"].shape, dtype=np.float32), dev)
+    av = T(rng.standard_normal((e, 3), dtype=np.float32), dev)
+    Y = ctp.spherical_harmonics(v, L)
+    dY = ctp.conv_tp_bwd(G, x, Y, w, g, L, ctp.Y_GIVEN)[2]
+    outs = [torch.empty_like(x), torch.empty_like(w), torch.empty_like(v),                 # frame bwd
+            torch.empty_like(x), torch.empty_like(w), torch.empty_like(Y),                 # atomic bwd
+            torch.empty_like(x), torch.empty_like(w), torch.empty_like(v), torch.empty_like(G)]   # dd vec
+    ws = torch.empty(3 * e * 16, device=dev)
+
+    def run():
+        ctp.conv_tp_bwd(G, x, v, w, g, L, ctp.VEC_GIVEN, dx=outs[0], dw=outs[1], dy=outs[2], algo=ctp.ALGO_FRAME)
+        ctp.conv_tp_bwd(G, x, Y, w, g, L, ctp.Y_GIVEN, dx=outs[3], dw=outs[4], dy=outs[5], algo=ctp.ALGO_ATOMIC)
+        ctp.conv_tp_bwd_bwd_vec(G, x, v, w, ax, aw, av, g, L, dY=dY, out=tuple(outs[6:]), workspace=ws)
+
+    print("graph capture frame bwd + atomic bwd + dd vec", flush=True)
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for k in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for q, (a, b) in enumerate(zip(outs, ref)):
+            if q == 3:
+                close("atomic dx", host(a), host(b))
+            else:
+                assert torch.equal(a, b), (k, q)
+
+
 def test_random_shapes_every_entry_point(ctp, dev):
     """Seeded random problems (independent degrees, channel count including
     ragged ones and two backward channel tiles, graph size with empty rows,
