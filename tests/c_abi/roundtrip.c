@@ -2,13 +2,14 @@
  *
  * TEST INFRASTRUCTURE: reads a problem and its inputs from a binary file,
  * allocates device memory with the HIP runtime, runs conv_tp_build_transpose,
- * conv_tp_fwd and conv_tp_bwd (or conv_tp_bwd_msg) on the null stream, and
+ * conv_tp_fwd and conv_tp_bwd (or conv_tp_bwd_msg) with the given algo on
+ * the null stream, and
  * writes the outputs to a binary file.  tests/test_gpu_c_abi.py compares them
  * with the oracle.
  *
  *   roundtrip IN OUT
  *
- * IN : int32 head[8] = {N, E, C, L, y_mode, variant, use_msg, 0}, then
+ * IN : int32 head[8] = {N, E, C, L, y_mode, variant, use_msg, algo}, then
  *      x[N][D][C] f32, y[E][S] f32 (S = D or 3), w[E][P][C] f32,
  *      G[N][D_out][C] f32, row_ptr[N+1] i32, senders[E] i32
  * OUT: out[N][D_out][C], dx[N][D][C], dw[E][P][C], dy[E][S] (f32), then
@@ -112,7 +113,7 @@ int main(int argc, char **argv) {
     prob.channels = head[2];
     prob.l_in = prob.l_sh = prob.l_out = head[3];
     prob.y_mode = head[4];
-    prob.algo = 0;
+    prob.algo = head[7];
     prob.variant = head[5];
 
     dx_in = to_device(x, N * D * C * sizeof(float));

@@ -1,8 +1,8 @@
 """The library driven from plain C: tests/c_abi/roundtrip (a C99 program
 built by the repository build entry point or `python tests/c_abi/build.py`) allocates
 device memory with the HIP runtime, builds the transpose and runs the
-forward and a backward through include/convtp.h; its outputs are compared
-with the oracle (transpose arrays bit-exact)."""
+forward and a backward (each algorithm) through include/convtp.h; its outputs
+are compared with the oracle (transpose arrays bit-exact)."""
 import os
 import subprocess
 
@@ -26,9 +26,12 @@ def _close(name, got, ref):
     assert scale > 0.0 and err <= 1e-4 * scale, f"{name}: max err {err:.3e} vs scale {scale:.3e}"
 
 
-@pytest.mark.parametrize("L,c,variant,y_mode,use_msg", [(2, 48, 0, 0, 0), (3, 128, 0, 1, 0), (3, 96, 1, 0, 1),
-                                                        (1, 16, 1, 1, 0), (2, 70, 0, 0, 1)])
-def test_c_program_roundtrip(tmp_path, L, c, variant, y_mode, use_msg):
+@pytest.mark.parametrize("L,c,variant,y_mode,use_msg,algo", [
+    (2, 48, 0, 0, 0, 0), (3, 128, 0, 1, 0, 0), (3, 96, 1, 0, 1, 0), (1, 16, 1, 1, 0, 0), (2, 70, 0, 0, 1, 0),
+    (3, 128, 0, 1, 0, 2),      # edge frame, forward and backward
+    (3, 96, 1, 0, 0, 1),       # atomics: edge-parallel forward, receiver-major backward
+])
+def test_c_program_roundtrip(tmp_path, L, c, variant, y_mode, use_msg, algo):
     if not os.path.exists(BIN):
         pytest.fail(f"{BIN} is missing: build it with `python tests/c_abi/build.py`")
     d = gen.poisson_small(70, c, L, mean_deg=9.0, seed=L + c)
@@ -40,13 +43,13 @@ def test_c_program_roundtrip(tmp_path, L, c, variant, y_mode, use_msg):
     vec = d["vec"].astype(np.float32)
     Y = osh.real_sh(L, vec.astype(np.float64)).astype(np.float32)
     yin = Y if y_mode == 0 else vec
-    head = np.array([n, e, c, L, y_mode, variant, use_msg, 0], dtype=np.int32)
+    head = np.array([n, e, c, L, y_mode, variant, use_msg, algo], dtype=np.int32)
     src, dst = tmp_path / "in.bin", tmp_path / "out.bin"
     with open(src, "wb") as f:
         for a in (head, d["x"].astype(np.float32), yin, w, G, d["row_ptr"].astype(np.int32),
                   d["senders"].astype(np.int32)):
             f.write(np.ascontiguousarray(a).tobytes())
-    print(f"roundtrip L={L} c={c} variant={variant} y_mode={y_mode} msg={use_msg}", flush=True)
+    print(f"roundtrip L={L} c={c} variant={variant} y_mode={y_mode} msg={use_msg} algo={algo}", flush=True)
     r = subprocess.run([BIN, str(src), str(dst)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     raw = np.fromfile(dst, dtype=np.uint8)
