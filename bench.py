@@ -579,7 +579,13 @@ def cpu_baseline(spec, sample_nodes):
     edges_per_s = e_sample / t
     gbs = edges_per_s * (step_bytes / E) / 1e9
     what = "forward + backward (dx, dw, dY)" if fb else "forward"
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": nt, "kind": "oracle",
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": nt, "kind": "oracle", "cpu_model": cpu_model,
             "edges_per_s": round(edges_per_s, 1), "seconds": round(t, 2),
             "forward_seconds": round(t_fwd, 2), "backward_seconds": round(t_bwd, 2),
             "sample": f"{what} over the {e_sample} in-edges of the first {len(rows)} receivers "
@@ -681,6 +687,7 @@ def main():
                for k in wl["kernel_bytes"]}
     tag = run_tag(args)
     traffic = committed_traffic(tag, dom)
+    wl["cfg"].setdefault("seed", 0)     # graphs and features drawn with seed 0 (fixed seeds elsewhere)
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_value, 4),
