@@ -487,7 +487,7 @@ def run_full(ctp, dev, n, c, L, y_mode, algo=0, bwd=False, seed=0, n_sample=48):
     del out
     if not bwd:
         return
-    dx, dw, dy = ctp.conv_tp_bwd(d["grad_out"], d["x"], yin, d["w"], g, L, y_mode)
+    dx, dw, dy = ctp.conv_tp_bwd(d["grad_out"], d["x"], yin, d["w"], g, L, y_mode, algo=algo)
     G_host = host(d["grad_out"])
     close("dx[sample]", host(dx[torch.as_tensor(rows, device=dev)]),
           _sub_dx(prob, rp, s, Yref, d["w"], G_host, rows))
@@ -510,6 +510,12 @@ def test_full_l2_forward(ctp, dev):
 def test_full_l3_forward_backward(ctp, dev, y_mode):
     """lmax=3, N=16384, C=128 (N*C = 2^21), forward and backward."""
     run_full(ctp, dev, 16384, 128, 3, y_mode, bwd=True)
+
+
+def test_full_l3_edge_frame_forward_backward(ctp, dev):
+    """lmax=3, N=16384, C=128, edge vectors, forward and backward in each
+    edge's frame (algo 2), as `bench.py --vec --frame` times them."""
+    run_full(ctp, dev, 16384, 128, 3, 1, algo=2, bwd=True, seed=3)
 
 
 @pytest.mark.parametrize("c", gen.SWEEP_CHANNELS)
@@ -915,6 +921,11 @@ def test_bwd_msg_full_l3_sampled(ctp, dev):
     dx0, dw0, dy0 = ctp.conv_tp_bwd(G, d["x"], T(Y, dev), w, g, L, 0, variant=1)
     assert torch.equal(dw, dw0) and torch.equal(dy, dy0)
     close("dx vs conv_tp_bwd", host(dx), host(dx0))
+    # algo 1 (receiver-major, dx by atomics), as `bench.py --workload l3mace --bwd atomic` times it
+    dx1, dw1, dy1 = ctp.conv_tp_bwd(G, d["x"], T(Y, dev), w, g, L, 0, variant=1, algo=ctp.ALGO_ATOMIC)
+    assert torch.equal(dw1, dw) and torch.equal(dy1, dy)
+    close("dx (algo 1)[sample]", host(dx1[torch.as_tensor(rows, device=dev)]), _sub_dx(pr, rp, s, Yr, w, G_h, rows))
+    close("dx (algo 1) vs conv_tp_bwd_msg", host(dx1), host(dx))
 
 
 @pytest.mark.parametrize("variant", [0, 1])
