@@ -655,6 +655,39 @@ def test_double_bwd_full_l3_sampled(ctp, dev):
     close("g_y[sample]", host(gy[ei]), dY1 + dY3)
 
 
+def test_double_bwd_edge_vectors_full_l3(ctp, dev):
+    """lmax=3, N=16384, C=128, as `bench.py --workload l3ddvec` runs it: the
+    one-call edge-vector VJP of the VJP (first backward's dY given) equals,
+    bit for bit, its steps called one by one (harmonics, harmonic JVP, the
+    Y-given double backward sampled against the oracle above, second-order
+    term); g_vec is also checked on sampled edges against the oracle's
+    harmonic terms applied to the library's g_y and dY."""
+    n, c, L = 16384, 128, 3
+    d = gen.poisson_full(n, c, L, dev, seed=0)
+    rp, s = d["row_ptr"], d["senders"]
+    ax, aw, _ = gen.cotangents_full(d, dev, seed=0)
+    v = T(d["vec"], dev)
+    av = torch.randn(v.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev)
+    g = ctp.Graph(n, T(rp, dev), T(s, dev))
+    G, x, w = d["grad_out"], d["x"], d["w"]
+    print("double bwd edge vectors full l3", flush=True)
+    Y = ctp.spherical_harmonics(v, L)
+    dY = ctp.conv_tp_bwd(G, x, Y, w, g, L, ctp.Y_GIVEN)[2]
+    res = ctp.conv_tp_bwd_bwd_vec(G, x, v, w, ax, aw, av, g, L, dY=dY)
+    aY = ctp.spherical_harmonics_jvp(v, av, L)
+    gx, gw, gy, gG = ctp.conv_tp_bwd_bwd(G, x, Y, w, ax, aw, aY, g, L)
+    gv = ctp.spherical_harmonics_bwd_bwd(v, dY, av, gy, L)
+    for name, a, b in zip(("g_x", "g_w", "g_vec", "g_grad"), res, (gx, gw, gv, gG)):
+        assert torch.equal(a, b), name
+    rng = np.random.default_rng(8)
+    edges = np.sort(rng.choice(len(s), 256, replace=False))
+    ei = torch.as_tensor(edges, device=dev)
+    v64 = d["vec"][edges].astype(np.float64)
+    ref = (osh.vec_grad_from_sh_grad(L, v64, host(gy[ei]).astype(np.float64))
+           + osh.vec_hess_term(L, v64, host(dY[ei]).astype(np.float64), host(av[ei]).astype(np.float64)))
+    close("g_vec[sample]", host(res[2][ei]), ref)
+
+
 # ------------------------------------------------------------ MACE variant (natural parity, slots)
 
 
