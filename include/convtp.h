@@ -42,7 +42,9 @@
  * Memory and ownership.  Array pointers are DEVICE pointers unless marked
  * host.  The caller allocates and owns every buffer; the library never
  * allocates, frees or retains caller memory.  It owns only a few bytes of
- * per-device state for conv_tp_check_graph.  Outputs are overwritten, never
+ * per-device state for conv_tp_check_graph and the fixed scratch array of
+ * conv_tp_bwd_msg_noalloc (256 MiB of device memory on each GPU the library
+ * is loaded on, held until the process ends).  Outputs are overwritten, never
  * accumulated into; rows with no edges get exact zeros.  Inputs and outputs
  * must not overlap.
  *
