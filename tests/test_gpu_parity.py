@@ -282,7 +282,8 @@ def test_random_shapes_every_entry_point(ctp, dev):
     """Seeded random problems (independent degrees, channel count including
     ragged ones and two backward channel tiles, graph size with empty rows,
     both Y modes, both variants) through every conv entry point: forward algos
-    0/1/2, backward, message backward and dY alone, each against the oracle."""
+    0/1/2, backward algos 0/1/2, message backward and dY alone, each against
+    the oracle."""
     rng = np.random.default_rng(2024)
     for case in range(32):
         deg = tuple(int(v) for v in rng.integers(0, 4, size=3))
@@ -316,7 +317,11 @@ def test_random_shapes_every_entry_point(ctp, dev):
         dx_ref = oc.bwd_dx(pr, Yref, d["w"], d["grad_out"], sp, pe, sr)
         dw_ref, dY_ref = oc.bwd_edges(pr, d["x"], Yref, d["w"], d["grad_out"], d["row_ptr"], d["senders"])
         dy_ref = dY_ref if y_mode == 0 else osh.vec_grad_from_sh_grad(L, d["vec"].astype(np.float64), dY_ref)
-        for name, fn in (("bwd", ctp.conv_tp_bwd), ("bwd_msg", ctp.conv_tp_bwd_msg)):
+        bwds = [("bwd", ctp.conv_tp_bwd), ("bwd_msg", ctp.conv_tp_bwd_msg),
+                ("bwd algo 1", lambda *a, **k: ctp.conv_tp_bwd(*a, **k, algo=ctp.ALGO_ATOMIC))]
+        if y_mode == 1 and variant == 0:
+            bwds.append(("bwd algo 2", lambda *a, **k: ctp.conv_tp_bwd(*a, **k, algo=ctp.ALGO_FRAME)))
+        for name, fn in bwds:
             dx, dw, dy = fn(G, x, yv, w, g, deg, y_mode, variant=variant)
             close(f"{name} dx", host(dx), dx_ref, nonzero=nz)
             close(f"{name} dw", host(dw), dw_ref, nonzero=nz)
