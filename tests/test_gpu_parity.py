@@ -531,6 +531,106 @@ def test_full_channel_sweep(ctp, dev, c, algo):
     torch.cuda.empty_cache()
 
 
+class _DevRows:
+    """Rows of a device array fetched when indexed (fp64 on the host), mapped
+    by `fn` if given (edge vectors -> harmonics), so that the sampled oracle
+    helpers never copy a multi-GB array whole."""
+
+    def __init__(self, t, fn=None):
+        self.t, self.fn = t, fn
+
+    def __getitem__(self, idx):
+        i = torch.as_tensor(np.asarray(idx, dtype=np.int64), device=self.t.device)
+        a = host(self.t[i]).astype(np.float64)
+        return a if self.fn is None else self.fn(a)
+
+
+def test_offsets_beyond_int32(ctp, dev):
+    """lmax=3, C=2, 2^20 receivers of in-degree 40: E = 41.9M edges, so w and
+    dw hold E*P*C = 2.85e9 elements (11.4 GB) and the rows of the last edges
+    lie beyond 2^31 elements and 2^32 bytes.  Every entry point that indexes
+    edge rows (forward CSR and atomic; backward direct, atomic and through
+    messages; dY alone; the VJP of the VJP; edge vectors direct and in the
+    edge frame) is compared with the oracle on samples that include the last
+    receivers, the last edges and the senders of the last edges."""
+    n, deg, c, L = 1 << 20, 40, 2, 3
+    print("large offsets: inputs", flush=True)
+    d = gen.fixed_degree_large(n, deg, c, L, dev, seed=5)
+    rp, s, e = d["row_ptr"], d["senders"], d["n_edges"]
+    assert e * gen.num_paths(L) * c > 2**31
+    prob = oc.Problem(L, L, L)
+    x, w, G, Y, vec = d["x"], d["w"], d["grad_out"], d["y"], d["vec"]
+    rng = np.random.default_rng(17)
+    rows = np.unique(np.concatenate([np.arange(n - 6, n), rng.choice(n, 10, replace=False)]))
+    edges = np.unique(np.concatenate([np.arange(e - 12, e), rng.choice(e, 36, replace=False)]))
+    send_sel = np.unique(np.concatenate([s[e - 6:], rng.choice(n, 6, replace=False)]))
+    ri, si, ei = (torch.as_tensor(a, device=dev) for a in (rows, send_sel, edges))
+    x_h, G_h = host(x), host(G)
+    g = ctp.Graph(n, T(rp, dev), T(s, dev))
+    g.transpose
+
+    Yr = _DevRows(Y)
+    ref_out = _sub_fwd(prob, rp, s, Yr, w, x_h, rows)
+    ref_dx = _sub_dx(prob, rp, s, Yr, w, G_h, send_sel)
+    ref_dw, ref_dY = _sub_edges(prob, rp, s, Yr, w, x_h, G_h, edges)
+    for algo in (ctp.ALGO_CSR, ctp.ALGO_ATOMIC):
+        print(f"large offsets: forward algo {algo}", flush=True)
+        out = ctp.conv_tp_fwd(x, Y, w, g, L, ctp.Y_GIVEN, algo)
+        close(f"out[sample] algo {algo}", host(out[ri]), ref_out)
+        del out
+    bwds = (("bwd algo 0", lambda: ctp.conv_tp_bwd(G, x, Y, w, g, L)),
+            ("bwd algo 1", lambda: ctp.conv_tp_bwd(G, x, Y, w, g, L, algo=ctp.ALGO_ATOMIC)),
+            ("bwd_msg", lambda: ctp.conv_tp_bwd_msg(G, x, Y, w, g, L)))
+    for name, run in bwds:
+        print(f"large offsets: {name}", flush=True)
+        dx, dw, dy = run()
+        close(f"dx[sample] {name}", host(dx[si]), ref_dx)
+        close(f"dw[sample] {name}", host(dw[ei]), ref_dw)
+        close(f"dY[sample] {name}", host(dy[ei]), ref_dY)
+        del dx, dw, dy
+        torch.cuda.empty_cache()
+    print("large offsets: bwd_dy", flush=True)
+    close("dY[sample] bwd_dy", host(ctp.conv_tp_bwd_dy(G, x, w, g, L)[ei]), ref_dY)
+
+    print("large offsets: double backward", flush=True)
+    ax = gen.normal_tensor(x.shape, 5, 26, dev)
+    aw = gen.normal_tensor(w.shape, 5, 27, dev)
+    aY = gen.normal_tensor(Y.shape, 5, 28, dev)
+    gx, gw, gy, gG = ctp.conv_tp_bwd_bwd(G, x, Y, w, ax, aw, aY, g, L)
+    ax_h, aYr = host(ax), _DevRows(aY)
+    close("g_grad[sample]", host(gG[ri]),
+          _sub_fwd(prob, rp, s, Yr, w, ax_h, rows) + _sub_fwd(prob, rp, s, Yr, aw, x_h, rows)
+          + _sub_fwd(prob, rp, s, aYr, w, x_h, rows))
+    close("g_x[sample]", host(gx[si]),
+          _sub_dx(prob, rp, s, Yr, aw, G_h, send_sel) + _sub_dx(prob, rp, s, aYr, w, G_h, send_sel))
+    dw1, dY1 = _sub_edges(prob, rp, s, Yr, w, ax_h, G_h, edges)
+    dw2, _ = _sub_edges(prob, rp, s, aYr, w, x_h, G_h, edges)
+    _, dY3 = _sub_edges(prob, rp, s, Yr, aw, x_h, G_h, edges)
+    close("g_w[sample]", host(gw[ei]), dw1 + dw2)
+    close("g_y[sample]", host(gy[ei]), dY1 + dY3)
+    del ax, aw, aY, gx, gw, gy, gG, Y
+    torch.cuda.empty_cache()
+
+    Vr = _DevRows(vec, lambda v: osh.real_sh(L, v))
+    ref_out = _sub_fwd(prob, rp, s, Vr, w, x_h, rows)
+    ref_dx = _sub_dx(prob, rp, s, Vr, w, G_h, send_sel)
+    ref_dw, ref_dY = _sub_edges(prob, rp, s, Vr, w, x_h, G_h, edges)
+    ref_dvec = osh.vec_grad_from_sh_grad(L, host(vec[ei]).astype(np.float64), ref_dY)
+    for algo in (ctp.ALGO_CSR, ctp.ALGO_FRAME):
+        print(f"large offsets: edge vectors algo {algo}", flush=True)
+        out = ctp.conv_tp_fwd(x, vec, w, g, L, ctp.VEC_GIVEN, algo)
+        close(f"out[sample] vec algo {algo}", host(out[ri]), ref_out)
+        del out
+        dx, dw, dv = ctp.conv_tp_bwd(G, x, vec, w, g, L, ctp.VEC_GIVEN, algo=algo)
+        close(f"dx[sample] vec algo {algo}", host(dx[si]), ref_dx)
+        close(f"dw[sample] vec algo {algo}", host(dw[ei]), ref_dw)
+        close(f"dvec[sample] vec algo {algo}", host(dv[ei]), ref_dvec)
+        del dx, dw, dv
+        torch.cuda.empty_cache()
+    del d, x, w, G, vec
+    torch.cuda.empty_cache()
+
+
 def test_water_box_two_layers(ctp, dev):
     """1503 atoms, 83,325 padded edges, C=128, lmax=3, vec mode: two chained
     layers forward, then backward to the edge vectors (sum of both layers)."""

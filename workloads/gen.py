@@ -202,6 +202,32 @@ def poisson_full(n_nodes: int, channels: int, lmax: int, device, mean_deg: float
     return out
 
 
+def fixed_degree_large(n_nodes: int, deg: int, channels: int, lmax: int, device, seed: int = 0):
+    """Large-offset workload: every receiver draws `deg` senders uniformly from
+    the other nodes (host PCG64, as poisson_graph), so E = n_nodes * deg; x, w,
+    G, a Y-given array (standard normal values, not harmonics: the Y-given
+    operation takes any Y) and Gaussian edge vectors are drawn on `device`
+    (tags 21..25).  Sized so that E * P * C passes 2^31, the edge rows of w and
+    dw lie beyond 32-bit element offsets."""
+    rng = rng_for(seed)
+    e = n_nodes * deg
+    if e >= 2**31:
+        raise ValueError("edge count does not fit int32")
+    row_ptr = (np.arange(n_nodes + 1, dtype=np.int64) * deg).astype(np.int32)
+    recv = np.repeat(np.arange(n_nodes, dtype=np.int32), deg)
+    s = rng.integers(0, n_nodes - 1, size=e, dtype=np.int32)
+    s += (s >= recv)
+    del recv
+    d = (lmax + 1) ** 2
+    return dict(name=f"fixed_n{n_nodes}_deg{deg}_c{channels}_l{lmax}", n_nodes=n_nodes, n_edges=e,
+                channels=channels, lmax=lmax, row_ptr=row_ptr, senders=s,
+                x=normal_tensor((n_nodes, d, channels), seed, 21, device),
+                w=normal_tensor((e, num_paths(lmax), channels), seed, 22, device),
+                grad_out=normal_tensor((n_nodes, d, channels), seed, 23, device),
+                y=normal_tensor((e, d), seed, 24, device),
+                vec=normal_tensor((e, 3), seed, 25, device))
+
+
 def water_box_graph(seed: int = 0, n_atoms: int = 1503, box: float = 25.0,
                     cutoff: float = 5.0, n_edges: int = 83325):
     """Periodic random 'water box': CSR neighbour list padded to n_edges.
