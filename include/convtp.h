@@ -38,6 +38,8 @@
  *   send_ptr[N+1], send_perm[E], send_recv[E]: the same edges grouped by
  *   sender, stable in CSR edge id (from conv_tp_build_transpose).
  *   D_l = (l+1)^2, P = conv_tp_num_paths(...).
+ *   N and E are int32, but element offsets are formed in 64 bits, so any
+ *   array may hold more than 2^31 elements (w and dw of E*P*C elements).
  *
  * Memory and ownership.  Array pointers are DEVICE pointers unless marked
  * host.  The caller allocates and owns every buffer; the library never
