@@ -101,11 +101,22 @@ __device__ __forceinline__ void load_edge_operands(float (&xv)[S::D1][CPL], floa
 
 // ------------------------------------------------------------ K1: CSR forward (deterministic)
 //
-// Rotating prefetch: right after path p of edge e has consumed w[e, p], the
-// same registers receive w[e+1, p]; each x block is refilled with the next
-// sender's row after its last use.  Every load thus has about one edge of
-// arithmetic to arrive, with no second register set.  The next edge's Y is
+// Rotating prefetch through a window of R w registers (R divides P): path p
+// reads slot p % R, and right after it has consumed w[e, p] that slot receives
+// the row R paths ahead, w[e, p + R] or, past the edge's last path,
+// w[e+1, p + R - P].  With R = P every load has a whole edge of arithmetic to
+// arrive; with R = P/2 half an edge, for half the registers (at lmax 3:
+// 77 instead of 110 VGPRs, six waves per SIMD instead of four, measured 2%
+// faster; a window of two paths was 15% slower).  Each x block is refilled
+// with the next sender's row after its last use.  The next edge's Y is
 // loaded early and its T is built into the other LDS buffer after compute.
+
+// Window of w registers: half the paths when there are enough of them (P even
+// and at least 32) for half an edge of arithmetic to cover a load, else all.
+template <class S>
+constexpr int fwd_window() {
+    return (S::P >= 32 && S::P % 2 == 0) ? S::P / 2 : S::P;
+}
 
 template <class S>
 constexpr bool last_path_of_l1(int p) {
@@ -113,10 +124,15 @@ constexpr bool last_path_of_l1(int p) {
 }
 
 // Path loop of one edge with refills for the next edge.
+// cw: the current edge's w row; nx, nw: the next edge's x and w rows (nvoff:
+// out of range after the last edge, so those loads return 0).
 template <class S, int CPL>
 __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::DO][CPL], float (&xv)[S::D1][CPL],
-                                                    float (&wv)[S::P][CPL], const float* sT, rsrc_t nx,
-                                                    rsrc_t nw, uint32_t nvoff, int C) {
+                                                    float (&wv)[fwd_window<S>()][CPL], const float* sT,
+                                                    rsrc_t cw, uint32_t voff, rsrc_t nx, rsrc_t nw,
+                                                    uint32_t nvoff, int C) {
+    constexpr int R = fwd_window<S>();
+    static_assert(S::P % R == 0, "the window must divide the path count");
     static_for<S::P>([&](auto pI) __attribute__((always_inline)) {
         constexpr int p = decltype(pI)::value;
         constexpr PathL q = S::paths[p];
@@ -128,7 +144,7 @@ __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::DO][CPL], fl
 #pragma unroll
             for (int a = 0; a < n1; ++a)
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) xs[a][c] = wv[p][c] * xv[o1 + a][c];
+                for (int c = 0; c < CPL; ++c) xs[a][c] = wv[p % R][c] * xv[o1 + a][c];
             static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
                 constexpr int t = t0 + decltype(tI)::value;
                 constexpr TSlot s = S::slots[t];
@@ -154,16 +170,20 @@ __device__ __forceinline__ void edge_forward_refill(float (&acc)[S::DO][CPL], fl
 #pragma unroll
             for (int k = 0; k < n3; ++k)
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) acc[o3 + k][c] = __builtin_fmaf(wv[p][c], u[k][c], acc[o3 + k][c]);
+                for (int c = 0; c < CPL; ++c) acc[o3 + k][c] = __builtin_fmaf(wv[p % R][c], u[k][c], acc[o3 + k][c]);
         }
         // keep this path's arithmetic here (pure code would otherwise sink to the loop latch)
 #pragma unroll
         for (int k = 0; k < n3; ++k)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) pin_f32(acc[o3 + k][c]);
-        // refills for the next edge (loads return 0 when there is none)
+        // refills: w R paths ahead (this edge's row, else the next edge's), x
+        // blocks for the next edge after their last use
         const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
-        bload<CPL, kStream>(nw, nvoff, (uint32_t)p * c4, wv[p]);
+        if constexpr (p + R < S::P)
+            bload<CPL, kStream>(cw, voff, (uint32_t)(p + R) * c4, wv[p % R]);
+        else
+            bload<CPL, kStream>(nw, nvoff, (uint32_t)(p + R - S::P) * c4, wv[p % R]);
         if constexpr (last_path_of_l1<S>(p)) {
 #pragma unroll
             for (int a = 0; a < n1; ++a) bload<CPL>(nx, nvoff, (uint32_t)(o1 + a) * c4, xv[o1 + a]);
@@ -211,8 +231,18 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
             if constexpr (VEC)
                 if (tid < 16) sSh[tid] = sh_tab().k[tid];
         }
-        float xv[D1][CPL], wv[P][CPL];
-        load_edge_operands<S, CPL>(xv, wv, x, w, senders[e0], e0, C, voff);
+        constexpr int R = fwd_window<S>();
+        float xv[D1][CPL], wv[R][CPL];
+        {
+            // the first edge's x row and the first R paths of its w row
+            const rsrc_t xr = make_row(x + (long)senders[e0] * D1 * C, (long)D1 * C);
+            const rsrc_t wr = make_row(w + (long)e0 * P * C, (long)P * C);
+            const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+#pragma unroll
+            for (int d = 0; d < D1; ++d) bload<CPL>(xr, voff, (uint32_t)d * c4, xv[d]);
+#pragma unroll
+            for (int p = 0; p < R; ++p) bload<CPL, kStream>(wr, voff, (uint32_t)p * c4, wv[p]);
+        }
         const float y0 = sh_value<D2, VEC>(yv, e0, tid);
         if (tid < D2) sY[0][tid] = y0;
         __syncthreads();
@@ -233,7 +263,8 @@ k_fwd_csr(int C, const float* __restrict__ x, const float* __restrict__ yv, cons
             } else {
                 ynext = sh_value<D2, VEC>(yv, en, tid);
             }
-            edge_forward_refill<S, CPL>(acc, xv, wv, sT[buf], nx, nw, nvoff, C);
+            const rsrc_t cw = make_row(w + (long)e * P * C, (long)P * C);
+            edge_forward_refill<S, CPL>(acc, xv, wv, sT[buf], cw, voff, nx, nw, nvoff, C);
             if (has_next) {
                 if (tid < D2) sY[buf ^ 1][tid] = ynext;
                 __syncthreads();
