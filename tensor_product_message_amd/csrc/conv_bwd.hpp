@@ -61,6 +61,59 @@ __device__ __forceinline__ void load_node_edge_rows(float (&nv)[D], float (&wv)[
     }
 }
 
+// Paths in the order edge_backward consumes them (group by group), and back.
+template <class S>
+constexpr int path_at_pos(int k) {
+    for (int g = 0; g < S::NG; ++g) {
+        if (k < S::groups[g].n) return S::groups[g].p[k];
+        k -= S::groups[g].n;
+    }
+    return -1;
+}
+template <class S>
+constexpr int pos_of_path(int p) {
+    int k = 0;
+    for (int g = 0; g < S::NG; ++g)
+        for (int i = 0; i < S::groups[g].n; ++i, ++k)
+            if (S::groups[g].p[i] == p) return k;
+    return -1;
+}
+template <class S>
+constexpr int group_pos0(int g) {
+    int k = 0;
+    for (int i = 0; i < g; ++i) k += S::groups[i].n;
+    return k;
+}
+
+// Window of w registers of the sender-major backward: half the paths when
+// there are enough of them (P even and at least 32), else all (see
+// edge_backward).
+template <class S>
+constexpr int bwd_window() {
+    return (S::P >= 32 && S::P % 2 == 0) ? S::P / 2 : S::P;
+}
+
+// Register of path p's w: with the whole row (R = P) index p, else the
+// path's position in consumption order modulo R.
+template <class S, int R>
+constexpr int w_slot(int p) {
+    return R == S::P ? p : pos_of_path<S>(p) % R;
+}
+
+// G row of receiver n alone.
+template <int D>
+__device__ __forceinline__ void load_node_row(float (&nv)[D], const float* __restrict__ node, long n, int C,
+                                              uint32_t voff) {
+    const rsrc_t nr = make_row(node + n * D * C, (long)D * C);
+    const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        float t[1];
+        bload<1>(nr, voff, (uint32_t)d * c4, t);
+        nv[d] = t[0];
+    }
+}
+
 // One edge of the backward, given T = T(Y_e) in LDS, the sender's row x, the
 // receiver's row g of G and the edge's row w (one channel per lane):
 //   v_p = T_p^T g,  dw[e,p] = x . v_p (stored through dwr),  dxa += w_p v_p,
@@ -69,19 +122,30 @@ __device__ __forceinline__ void load_node_edge_rows(float (&nv)[D], float (&wv)[
 // dw_p and dx for its paths, then B_p from the products x[l1 m1] g[l3 m3]
 // formed m1 by m1 and shared by the group's paths.  Scheduling barriers after
 // each path and group bound register lifetimes.
-template <class S>
+// w: with R = P the caller loads the whole row (wv[p] = w[e,p]) and cw, nw,
+// nvoff are unused.  With R < P (R divides P) wv is a window: the path at
+// consumption position k reads register k mod R, and after each group its
+// registers receive the rows R positions ahead, from this edge's row cw or,
+// past the last position, from the next edge's row nw (nvoff out of range
+// after the last edge: the loads return 0).  Each load then has about half an
+// edge of arithmetic to arrive instead of the dY reduction between edges.
+template <class S, int R>
 __device__ __forceinline__ void edge_backward(const float* T, const float (&xv)[S::D1], const float (&gv)[S::DO],
-                                              const float (&wv)[S::P], rsrc_t dwr, uint32_t voff, int C,
-                                              float (&dxa)[S::D1], float (&dya)[16]) {
+                                              float (&wv)[R], rsrc_t dwr, uint32_t voff, int C,
+                                              float (&dxa)[S::D1], float (&dya)[16], rsrc_t cw, rsrc_t nw,
+                                              uint32_t nvoff) {
+    static_assert(S::P % R == 0, "the window must divide the path count");
     constexpr bool kBig = S::P >= 20;   // bound register lifetimes more tightly in the large cases
     static_for<S::NG>([&](auto gI) __attribute__((always_inline)) {
-        constexpr PathGroup pp = S::groups[decltype(gI)::value];
+        constexpr int gidx = decltype(gI)::value;
+        constexpr PathGroup pp = S::groups[gidx];
         constexpr int l1 = pp.l1, l3 = pp.l3;
         constexpr int n1 = 2 * l1 + 1, n3 = 2 * l3 + 1;
         constexpr int o1 = l1 * l1, o3 = pp.o3;   // o3: the group's block of G
         // (a) v_p = T_p^T g, dw_p = x . v_p, dx += w_p v_p
         static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
             constexpr int p = pp.p[decltype(kI)::value];
+            constexpr int ws = w_slot<S, R>(p);   // constexpr: folded, never a runtime index
             constexpr int t0 = S::slot_begin[p], t1 = S::slot_begin[p + 1];
             float v[n1];
             static_for<t1 - t0>([&](auto tI) __attribute__((always_inline)) {
@@ -100,7 +164,7 @@ __device__ __forceinline__ void edge_backward(const float* T, const float (&xv)[
             bstore<1, kStream>(dwr, voff, (uint32_t)p * opaque_u32((uint32_t)C * 4u), dwv);
 #pragma unroll
             for (int a = 0; a < n1; ++a) {
-                dxa[o1 + a] = __builtin_fmaf(wv[p], v[a], dxa[o1 + a]);
+                dxa[o1 + a] = __builtin_fmaf(wv[ws], v[a], dxa[o1 + a]);
                 pin_f32(dxa[o1 + a]);
             }
             if constexpr (kBig) __builtin_amdgcn_sched_barrier(0);
@@ -133,10 +197,31 @@ __device__ __forceinline__ void edge_backward(const float* T, const float (&xv)[
             constexpr int kk = decltype(kI)::value;
             constexpr int p = pp.p[kk];
             constexpr int n2 = 2 * S::paths[p].l2 + 1, o2 = S::paths[p].l2 * S::paths[p].l2;
+            constexpr int ws = w_slot<S, R>(p);
 #pragma unroll
-            for (int b = 0; b < n2; ++b) dya[o2 + b] = __builtin_fmaf(wv[p], B[kk][b], dya[o2 + b]);
+            for (int b = 0; b < n2; ++b) dya[o2 + b] = __builtin_fmaf(wv[ws], B[kk][b], dya[o2 + b]);
         });
+        if constexpr (R < S::P) {
+#pragma unroll
+            for (int d = 0; d < 16; ++d) pin_f32(dya[d]);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (R < S::P) {
+            // the group's w registers are free: the rows R positions ahead
+            const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+            static_for<pp.n>([&](auto kI) __attribute__((always_inline)) {
+                constexpr int k = group_pos0<S>(gidx) + decltype(kI)::value;
+                constexpr int q = k + R;
+                constexpr int pq = path_at_pos<S>(q < S::P ? q : q - S::P);
+                float t[1];
+                if constexpr (q < S::P)
+                    bload<1, kStream>(cw, voff, (uint32_t)pq * c4, t);
+                else
+                    bload<1, kStream>(nw, nvoff, (uint32_t)pq * c4, t);
+                wv[k % R] = t[0];
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        }
     });
 }
 
@@ -260,25 +345,47 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
             if constexpr (VEC)
                 if (tid < 16) sSh[tid] = sh_tab().k[tid];
         }
-        float gv[D3], wv[P];
+        constexpr int R = bwd_window<S>();
+        float gv[D3], wv[R];
         long e = send_perm[k0];
         const float y0 = sh_load<D2, VEC>(yv, e, tid);
-        load_node_edge_rows<D3, P>(gv, wv, G, w, send_recv[k0], e, C, voff);
+        if constexpr (R == P) {
+            load_node_edge_rows<D3, P>(gv, wv, G, w, send_recv[k0], e, C, voff);
+        } else {
+            // G row and the first R positions of the w row
+            load_node_row<D3>(gv, G, send_recv[k0], C, voff);
+            const rsrc_t wr = make_row(w + e * P * C, (long)P * C);
+            const uint32_t c4 = opaque_u32((uint32_t)C * 4u);
+            static_for<R>([&](auto kI) __attribute__((always_inline)) {
+                constexpr int pk = path_at_pos<S>(decltype(kI)::value);
+                float t[1];
+                bload<1, kStream>(wr, voff, (uint32_t)pk * c4, t);
+                wv[decltype(kI)::value] = t[0];
+            });
+        }
         if (tid < D2) sY[0][tid] = y0;
         __syncthreads();
         build_T_lds<S>(sT[0], sY[0], sTab, tid, nth);
         __syncthreads();
 
-        // Per out-edge k: compute with T(k) and the rows already in registers;
-        // then load the rows of edge k+1 into the same registers, reduce dY,
-        // and build T(k+1) in the other buffer while those loads are in flight.
+        // Per out-edge k: compute with T(k) and the rows already in registers
+        // (with a w window, w rows of this and the next edge are loaded during
+        // the arithmetic); then load the G row (and with R = P the w row) of
+        // edge k+1 into the same registers, reduce dY, and build T(k+1) in the
+        // other buffer while those loads are in flight.
         for (int k = k0; k < k1; ++k) {
             const int buf = (k - k0) & 1;
             const bool has_next = k + 1 < k1;
+            const int kn = has_next ? k + 1 : k;
             float dya[16];
 #pragma unroll
             for (int d = 0; d < 16; ++d) dya[d] = 0.0f;
-            edge_backward<S>(sT[buf], xv, gv, wv, make_row(dw + e * P * C, (long)P * C), voff, C, dxa, dya);
+            {
+                const rsrc_t cw = make_row(w + e * P * C, (long)P * C);
+                const rsrc_t nw = make_row(w + (long)send_perm[kn] * P * C, (long)P * C);
+                edge_backward<S, R>(sT[buf], xv, gv, wv, make_row(dw + e * P * C, (long)P * C), voff, C, dxa, dya,
+                                    cw, nw, has_next ? voff : kOffLane);
+            }
             // rows of the next edge into the registers just freed (unconditional:
             // after the last edge the loads use an out-of-range offset and return 0).
             // The dY sums are pinned first so the loads cannot be hoisted into the
@@ -286,14 +393,16 @@ k_bwd_sender(int C, const float* __restrict__ G, const float* __restrict__ x, co
 #pragma unroll
             for (int d = 0; d < D2; ++d) pin_f32(dya[d]);
             const long e_cur = e;
-            const int kn = has_next ? k + 1 : k;
             e = send_perm[kn];
             // A fresh copy of the thread index each edge keeps the address
             // arithmetic below from being hoisted out of the loop, where it would
             // hold registers through the arithmetic above.
             const int tt = (int)opaque_lane((uint32_t)tid);
             const float ynext = next_y<D2, VEC>(yv, e, tt, sSh);
-            load_node_edge_rows<D3, P>(gv, wv, G, w, send_recv[kn], e, C, has_next ? voff : kOffLane);
+            if constexpr (R == P)
+                load_node_edge_rows<D3, P>(gv, wv, G, w, send_recv[kn], e, C, has_next ? voff : kOffLane);
+            else
+                load_node_row<D3>(gv, G, send_recv[kn], C, has_next ? voff : kOffLane);
             __builtin_amdgcn_sched_barrier(0);
             edge_dy_finish<S, VEC>(dya, sRed, sT[buf ^ 1], sY[buf ^ 1], sTab, sSh, has_next, ynext, tt, nth, nwaves,
                                    yv, e_cur, dyv, dy_atomic != 0);
@@ -379,7 +488,10 @@ k_bwd_recv(int C, const float* __restrict__ G, const float* __restrict__ x, cons
         for (int d = 0; d < D1; ++d) mx[d] = 0.0f;
 #pragma unroll
         for (int d = 0; d < 16; ++d) dya[d] = 0.0f;
-        edge_backward<S>(sT[buf], xv, gv, wv, make_row(dw + e * P * C, (long)P * C), voff, C, mx, dya);
+        {
+            const rsrc_t dwr = make_row(dw + e * P * C, (long)P * C);
+            edge_backward<S, P>(sT[buf], xv, gv, wv, dwr, voff, C, mx, dya, dwr, dwr, kOffLane);   // whole w rows
+        }
         if constexpr (ATOMIC_DX) {
             if (c0 < C) {
                 float* o = msg + (long)senders[e] * D1 * C + c0;   // msg = dx here
